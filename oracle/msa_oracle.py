@@ -1,0 +1,380 @@
+"""fp64 CPU oracle for causal sliding-window + mean-pooled-landmark attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package may import, call or
+execute this module; only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path: it uses numpy only.
+
+What is computed (the pattern the pages call Flash-MSA, made precise):
+
+* "Scaling GPU Cluster for Million Token Context", section "Why Sparse
+  Attention Changes the Game": each query attends to a local window of
+  recent tokens plus a small set of landmark tokens that summarise distant
+  context; section "What is Flash-MSA Sparse Attention in GPU Clusters?":
+  both parts are computed in one fused pass.
+* "Training at 1M+ Token Context ...", Block-Sparse Flash Attention
+  paragraph: distant context is represented by compression tokens, local
+  tokens by a sliding window.
+
+Readings taken where the pages leave the step open:
+
+* A landmark b is the plain mean of K and V over block b of L = n / G
+  consecutive positions (no learned projection).
+* Query i sees key j iff i - w < j <= i (w keys including itself, clipped at
+  position 0), and sees landmark b iff the block's last position
+  (b+1)*L - 1 is at or before i - w.  Blocks that straddle the window edge
+  are not visible.
+* Window keys and visible landmarks share ONE softmax with one scale
+  (1/sqrt(d) by default); the output is O_i and LSE_i = m_i + ln(l_i) with
+  the natural log, in units of the scaled score.
+* Query head h reads KV head h // (Hq / Hkv).
+* Decode is the same computation for the single row i = ctx - 1.  The
+  split form partitions the ordered visible list (landmarks ascending, then
+  window keys ascending) into S contiguous chunks of ceil(E / S) entries and
+  merges the per-chunk results by their log-sum-exp, which is the one-GPU
+  form of the softmax-statistics aggregation in the Ring Attention paragraph
+  of the "Training at 1M+ Token Context" page.
+
+Every predicate below is evaluated by explicit comparisons; nothing uses a
+closed-form count of visible keys.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Step 1: landmarks (mean of each block of L = n / G positions)
+# ---------------------------------------------------------------------------
+
+def block_len(n: int, G: int) -> int:
+    """Block length L = n / G.  G must divide n."""
+    if G <= 0:
+        raise ValueError("no landmarks: G must be > 0 to have a block length")
+    if n % G:
+        raise ValueError(f"G={G} does not divide n={n}")
+    return n // G
+
+
+def pool(X: np.ndarray, G: int) -> np.ndarray:
+    """Landmarks of X [..., n, d]: [..., G, d], entry b = mean of rows
+    b*L .. b*L+L-1, in fp64."""
+    n = X.shape[-2]
+    L = block_len(n, G)
+    Xd = np.asarray(X, dtype=np.float64)
+    out = np.empty(Xd.shape[:-2] + (G, Xd.shape[-1]), dtype=np.float64)
+    for b in range(G):
+        out[..., b, :] = Xd[..., b * L:(b + 1) * L, :].mean(axis=-2)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 2: visibility predicates (explicit comparisons)
+# ---------------------------------------------------------------------------
+
+def window_visible(i, j, w: int):
+    """Key j lies in query i's causal window: i - w < j <= i."""
+    i = np.asarray(i)
+    j = np.asarray(j)
+    return (j <= i) & (j > i - w)
+
+
+def landmark_visible(i, b, L: int, w: int):
+    """Landmark b (positions b*L .. (b+1)*L-1) ends at or before i - w."""
+    i = np.asarray(i)
+    b = np.asarray(b)
+    return (b + 1) * L - 1 <= i - w
+
+
+def dense_masks(n: int, w: int, G: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Full boolean masks M_win [n, n] and M_lm [n, G] (small n only)."""
+    i = np.arange(n)[:, None]
+    m_win = window_visible(i, np.arange(n)[None, :], w)
+    if G:
+        m_lm = landmark_visible(i, np.arange(G)[None, :], block_len(n, G), w)
+    else:
+        m_lm = np.zeros((n, 0), dtype=bool)
+    return m_win, m_lm
+
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head h: consecutive groups of Hq / Hkv."""
+    return h // (Hq // Hkv)
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-4: scores, one softmax over the union, output and LSE
+# ---------------------------------------------------------------------------
+
+def _softmax_rows(S_win, M_win, S_lm, M_lm, V_span, V_lm):
+    """One softmax per row over the visible window scores and the visible
+    landmark scores together.  Returns (O [R, d], LSE [R])."""
+    S_win = np.where(M_win, S_win, NEG_INF)
+    S_lm = np.where(M_lm, S_lm, NEG_INF)
+    m = np.maximum(S_win.max(axis=1, initial=NEG_INF), S_lm.max(axis=1, initial=NEG_INF))
+    P_win = np.where(M_win, np.exp(S_win - m[:, None]), 0.0)
+    P_lm = np.where(M_lm, np.exp(S_lm - m[:, None]), 0.0)
+    l = P_win.sum(axis=1) + P_lm.sum(axis=1)
+    num = P_win @ V_span
+    if V_lm is not None and V_lm.shape[0]:
+        num = num + P_lm @ V_lm
+    O = num / l[:, None]
+    lse = m + np.log(l)
+    return O, lse
+
+
+def _row_groups(rows: np.ndarray, span: int) -> List[np.ndarray]:
+    """Split sorted rows into consecutive groups covering at most `span`
+    positions each (so that each group's key range stays small)."""
+    groups = []
+    start = 0
+    for k in range(1, len(rows) + 1):
+        if k == len(rows) or rows[k] - rows[start] >= span:
+            groups.append(rows[start:k])
+            start = k
+    return groups
+
+
+def attn(Q, K, V, w: int, G: int, scale: Optional[float] = None,
+         rows: Optional[Dict[int, np.ndarray]] = None,
+         Kbar: Optional[np.ndarray] = None, Vbar: Optional[np.ndarray] = None,
+         group_span: int = 512):
+    """Window + landmark attention, fp64.
+
+    Q [B, Hq, n, d]; K, V [B, Hkv, n, d].  ``rows`` maps a query head to the
+    sorted query rows to evaluate (default: every row of every head).  Kbar
+    and Vbar may be given (e.g. to feed landmarks pooled elsewhere);
+    otherwise they are the fp64 means of K and V.
+
+    Returns {head: (rows, O [B, R, d], LSE [B, R])}.
+
+    For each group of nearby rows the scores are formed against every key in
+    a range that strictly contains the rows' windows (one extra key of margin
+    on each side), and the window predicate decides visibility of each of
+    them; the landmark predicate is evaluated against every landmark.
+    """
+    if w < 1:
+        raise ValueError("window must be >= 1")
+    Q = np.asarray(Q)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if G:
+        L = block_len(n, G)
+        if Kbar is None:
+            Kbar = pool(K, G)
+        if Vbar is None:
+            Vbar = pool(V, G)
+    results = {}
+    heads = range(Hq) if rows is None else sorted(rows)
+    for h in heads:
+        g = kv_head(h, Hq, Hkv)
+        r_all = np.arange(n) if rows is None else np.asarray(rows[h], dtype=np.int64)
+        O = np.empty((B, len(r_all), d))
+        LSE = np.empty((B, len(r_all)))
+        pos = 0
+        for grp_rows in _row_groups(r_all, group_span):
+            lo = max(0, int(grp_rows[0]) - w)           # one below the lowest visible key
+            hi = min(n, int(grp_rows[-1]) + 2)          # one above the highest visible key
+            keys = np.arange(lo, hi)
+            M_win = window_visible(grp_rows[:, None], keys[None, :], w)
+            if G:
+                M_lm = landmark_visible(grp_rows[:, None], np.arange(G)[None, :], L, w)
+            for b in range(B):
+                q = np.asarray(Q[b, h, grp_rows], dtype=np.float64)
+                k_span = np.asarray(K[b, g, lo:hi], dtype=np.float64)
+                v_span = np.asarray(V[b, g, lo:hi], dtype=np.float64)
+                S_win = scale * (q @ k_span.T)
+                if G:
+                    kb = np.asarray(Kbar[b, g], dtype=np.float64)
+                    vb = np.asarray(Vbar[b, g], dtype=np.float64)
+                    S_lm = scale * (q @ kb.T)
+                    o, lse = _softmax_rows(S_win, M_win, S_lm, M_lm, v_span, vb)
+                else:
+                    empty = np.zeros((len(grp_rows), 0))
+                    o, lse = _softmax_rows(S_win, M_win, empty, empty.astype(bool), v_span, None)
+                O[b, pos:pos + len(grp_rows)] = o
+                LSE[b, pos:pos + len(grp_rows)] = lse
+            pos += len(grp_rows)
+        results[h] = (r_all, O, LSE)
+    return results
+
+
+def attn_dense(Q, K, V, w: int, G: int, scale: Optional[float] = None):
+    """All rows: O [B, Hq, n, d], LSE [B, Hq, n] (small n)."""
+    B, Hq, n, d = np.asarray(Q).shape
+    res = attn(Q, K, V, w, G, scale)
+    O = np.stack([res[h][1] for h in range(Hq)], axis=1)
+    LSE = np.stack([res[h][2] for h in range(Hq)], axis=1)
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# Step 5: integer artefacts derived from the masks
+# ---------------------------------------------------------------------------
+
+def row_plan(n: int, w: int, G: int, rows: Optional[np.ndarray] = None):
+    """For each row: the lowest visible window key and the number of visible
+    landmarks, both read off the explicit predicates.  Returns (win_lo,
+    lm_count) as int64 arrays over ``rows`` (default all rows)."""
+    r = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    win_lo = np.empty(len(r), dtype=np.int64)
+    lm_count = np.zeros(len(r), dtype=np.int64)
+    L = block_len(n, G) if G else 0
+    for s in range(0, len(r), 256):
+        rr = r[s:s + 256]
+        lo = max(0, int(rr.min()) - w)
+        keys = np.arange(lo, min(n, int(rr.max()) + 2))
+        M = window_visible(rr[:, None], keys[None, :], w)
+        win_lo[s:s + 256] = keys[np.argmax(M, axis=1)]
+        if G:
+            lm_count[s:s + 256] = landmark_visible(rr[:, None], np.arange(G)[None, :], L, w).sum(axis=1)
+    return win_lo, lm_count
+
+
+def tile_plan(n: int, w: int, G: int, BM: int, BN: int, q_tiles: Optional[Sequence[int]] = None):
+    """The block-sparse tile set for query tiles of BM rows and key tiles of
+    BN keys, read off the masks: a (query tile, key tile) pair is listed iff
+    some (row, key) in it is visible, and flagged interior iff every slot of
+    it is visible (slots past the last key or landmark count as invisible).
+
+    Returns a list of (t, kind, tile, interior) with kind 0 = landmark tile,
+    1 = window tile, ordered by t, then kind, then tile."""
+    T = -(-n // BM)
+    ts = range(T) if q_tiles is None else q_tiles
+    L = block_len(n, G) if G else 0
+    out = []
+    for t in ts:
+        rws = np.arange(t * BM, min(n, t * BM + BM))
+        if G:
+            for lt in range(-(-G // BN)):
+                b = np.arange(lt * BN, lt * BN + BN)
+                M = landmark_visible(rws[:, None], b[None, :], L, w) & (b[None, :] < G)
+                if M.any():
+                    out.append((t, 0, lt, bool(M.all())))
+        # candidate key tiles: those overlapping [first row - w, last row + 1]
+        k_lo = max(0, int(rws[0]) - w) // BN
+        k_hi = min(-(-n // BN) - 1, (int(rws[-1]) + 1) // BN)
+        for kt in range(k_lo, k_hi + 1):
+            j = np.arange(kt * BN, kt * BN + BN)
+            M = window_visible(rws[:, None], j[None, :], w) & (j[None, :] < n)
+            if M.any():
+                out.append((t, 1, kt, bool(M.all())))
+    return out
+
+
+def visible_pairs(n: int, w: int, G: int, chunk: int = 4096) -> Tuple[int, int]:
+    """Total visible (query, key) window pairs and (query, landmark) pairs
+    of one head, counted from the predicates."""
+    L = block_len(n, G) if G else 0
+    win = 0
+    lm = 0
+    for s in range(0, n, chunk):
+        rr = np.arange(s, min(n, s + chunk))
+        lo = max(0, s - w)
+        keys = np.arange(lo, min(n, int(rr[-1]) + 2))
+        win += int(window_visible(rr[:, None], keys[None, :], w).sum())
+        if G:
+            lm += int(landmark_visible(rr[:, None], np.arange(G)[None, :], L, w).sum())
+    return win, lm
+
+
+# ---------------------------------------------------------------------------
+# Step 6: decode (single row i = ctx-1) and its split / LSE-merge form
+# ---------------------------------------------------------------------------
+
+def visible_list(i: int, n: int, w: int, G: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Ordered visible entries of row i: the visible landmarks in block
+    order, then the visible window keys ascending.  Returns (kinds, idx):
+    kind 0 = landmark index, 1 = key position."""
+    L = block_len(n, G) if G else 0
+    lm = np.arange(G)
+    lm = lm[landmark_visible(i, lm, L, w)] if G else lm
+    keys = np.arange(max(0, i - w), min(n, i + 2))
+    keys = keys[window_visible(i, keys, w)]
+    kinds = np.concatenate([np.zeros(len(lm), np.int64), np.ones(len(keys), np.int64)])
+    return kinds, np.concatenate([lm, keys]).astype(np.int64)
+
+
+def chunk_bounds(E: int, S: int) -> np.ndarray:
+    """Chunk c covers entries [c*s, min(E, (c+1)*s)) with s = ceil(E/S)."""
+    s = -(-E // S) if E else 0
+    return np.array([min(E, c * s) for c in range(S + 1)], dtype=np.int64)
+
+
+def _entries(q, kc, vc, kb, vb, kinds, idx, scale):
+    """Scores and values of the listed entries for one (sequence, head)."""
+    d = q.shape[-1]
+    kmat = np.empty((len(idx), d))
+    vmat = np.empty((len(idx), d))
+    is_lm = kinds == 0
+    kmat[is_lm] = kb[idx[is_lm]]
+    vmat[is_lm] = vb[idx[is_lm]]
+    kmat[~is_lm] = kc[idx[~is_lm]]
+    vmat[~is_lm] = vc[idx[~is_lm]]
+    return scale * (kmat @ q), vmat
+
+
+def decode_partials(q, Kc, Vc, w: int, G: int, S: int, scale: Optional[float] = None,
+                    Kbar=None, Vbar=None, bounds: Optional[np.ndarray] = None):
+    """Per-chunk results of decode.  q [B, Hq, d], caches [B, Hkv, ctx, d].
+    Returns (o [S, B, Hq, d], lse [S, B, Hq]); an empty chunk has lse = -inf
+    and o = 0.  ``bounds`` overrides the chunk boundaries (length S+1)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, ctx = Kc.shape[1], Kc.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if G:
+        Kbar = pool(Kc, G) if Kbar is None else Kbar
+        Vbar = pool(Vc, G) if Vbar is None else Vbar
+    i = ctx - 1
+    kinds, idx = visible_list(i, ctx, w, G)
+    E = len(idx)
+    bnd = chunk_bounds(E, S) if bounds is None else np.asarray(bounds)
+    o = np.zeros((S, B, Hq, d))
+    lse = np.full((S, B, Hq), NEG_INF)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            kb = np.asarray(Kbar[b, g], np.float64) if G else np.zeros((0, d))
+            vb = np.asarray(Vbar[b, g], np.float64) if G else np.zeros((0, d))
+            s_all, v_all = _entries(q[b, h], np.asarray(Kc[b, g], np.float64),
+                                    np.asarray(Vc[b, g], np.float64), kb, vb, kinds, idx, scale)
+            for c in range(S):
+                a, e = int(bnd[c]), int(bnd[c + 1])
+                if e <= a:
+                    continue
+                s = s_all[a:e]
+                m = s.max()
+                p = np.exp(s - m)
+                l = p.sum()
+                o[c, b, h] = (p @ v_all[a:e]) / l
+                lse[c, b, h] = m + np.log(l)
+    return o, lse
+
+
+def merge(o: np.ndarray, lse: np.ndarray):
+    """Combine chunk results: LSE = ln sum_c exp(lse_c), O = sum_c
+    exp(lse_c - LSE) o_c.  Empty chunks (lse_c = -inf) get weight 0."""
+    m = lse.max(axis=0)
+    wts = np.where(np.isfinite(lse), np.exp(lse - m), 0.0)
+    tot = wts.sum(axis=0)
+    LSE = m + np.log(tot)
+    O = (wts[..., None] * o).sum(axis=0) / tot[..., None]
+    return O, LSE
+
+
+def decode(q, Kc, Vc, w: int, G: int, scale: Optional[float] = None, Kbar=None, Vbar=None):
+    """Unsplit decode: one softmax over every visible entry of row ctx-1.
+    Returns (O [B, Hq, d], LSE [B, Hq])."""
+    o, lse = decode_partials(q, Kc, Vc, w, G, 1, scale, Kbar, Vbar)
+    return o[0], lse[0]

@@ -1,0 +1,107 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins catch every one: a pin set that passes a broken oracle pins nothing."""
+import numpy as np
+import pytest
+
+from oracle import msa_oracle as orc
+from tests import test_oracle_pins as pins
+
+
+def _window_wide(i, j, w):          # w+1 keys
+    return (np.asarray(j) <= np.asarray(i)) & (np.asarray(j) >= np.asarray(i) - w)
+
+
+def _window_no_self(i, j, w):       # excludes the query's own key
+    return (np.asarray(j) < np.asarray(i)) & (np.asarray(j) > np.asarray(i) - w - 1)
+
+
+def _landmark_exclusive(i, b, L, w):   # block must end strictly before i - w
+    return (np.asarray(b) + 1) * L - 1 < np.asarray(i) - w
+
+
+def _landmark_straddle(i, b, L, w):    # block only has to start before i - w
+    return np.asarray(b) * L <= np.asarray(i) - w
+
+
+def _pool_sum(X, G):                   # sum instead of mean
+    L = X.shape[-2] // G
+    return orc.__dict__["_orig_pool"](X, G) * L
+
+
+def _kv_head_mod(h, Hq, Hkv):          # interleaved instead of grouped
+    return h % Hkv
+
+
+def _softmax_drop_landmark_mass(S_win, M_win, S_lm, M_lm, V_span, V_lm):
+    S_win = np.where(M_win, S_win, -np.inf)
+    S_lm = np.where(M_lm, S_lm, -np.inf)
+    m = np.maximum(S_win.max(axis=1, initial=-np.inf), S_lm.max(axis=1, initial=-np.inf))
+    P_win = np.where(M_win, np.exp(S_win - m[:, None]), 0.0)
+    P_lm = np.where(M_lm, np.exp(S_lm - m[:, None]), 0.0)
+    l = P_win.sum(axis=1)                                  # landmark weights missing from l
+    num = P_win @ V_span
+    if V_lm is not None and V_lm.shape[0]:
+        num = num + P_lm @ V_lm
+    return num / l[:, None], m + np.log(l)
+
+
+def _softmax_log2(S_win, M_win, S_lm, M_lm, V_span, V_lm):
+    O, lse = orc.__dict__["_orig_softmax"](S_win, M_win, S_lm, M_lm, V_span, V_lm)
+    return O, lse / np.log(2.0)                            # LSE in the wrong base
+
+
+def _merge_unweighted(o, lse):
+    fin = np.isfinite(lse)
+    O = (o * fin[..., None]).sum(0) / fin.sum(0)[..., None]
+    return O, orc.__dict__["_orig_merge"](o, lse)[1]
+
+
+MUTANTS = {
+    "window_wide": ("window_visible", _window_wide),
+    "window_no_self": ("window_visible", _window_no_self),
+    "landmark_exclusive": ("landmark_visible", _landmark_exclusive),
+    "landmark_straddle": ("landmark_visible", _landmark_straddle),
+    "pool_sum": ("pool", _pool_sum),
+    "kv_head_mod": ("kv_head", _kv_head_mod),
+    "softmax_drop_landmark_mass": ("_softmax_rows", _softmax_drop_landmark_mass),
+    "lse_log2": ("_softmax_rows", _softmax_log2),
+    "merge_unweighted": ("merge", _merge_unweighted),
+}
+
+PIN_SET = [
+    lambda: pins.test_brute_force_mha(16, 3, 4),
+    lambda: pins.test_brute_force_gqa_batch(16, 3, 4),
+    lambda: pins.test_full_window_no_landmarks_is_causal_sdpa(64, 64),
+    lambda: pins.test_one_token_landmarks_give_causal_attention_for_any_window(7),
+    lambda: pins.test_golden_uniform_worked_example(),
+    lambda: pins.test_zero_keys_average_the_visible_values(128, 16, 8),
+    lambda: pins.test_key_shift_moves_lse_only(),
+    lambda: pins.test_pool_constant_blocks_and_bruteforce(),
+    lambda: pins.test_split_merge_any_partition(),
+    lambda: pins.test_decode_equals_prefill_last_row(256, 64, 16),
+    lambda: pins.test_window_one_no_landmarks_is_identity(),
+]
+
+
+def _failures():
+    n = 0
+    for pin in PIN_SET:
+        try:
+            pin()
+        except AssertionError:
+            n += 1
+    return n
+
+
+def test_unmutated_oracle_passes_the_pin_set():
+    assert _failures() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setitem(orc.__dict__, "_orig_pool", orc.pool)
+    monkeypatch.setitem(orc.__dict__, "_orig_softmax", orc._softmax_rows)
+    monkeypatch.setitem(orc.__dict__, "_orig_merge", orc.merge)
+    monkeypatch.setattr(orc, attr, fn)
+    assert _failures() > 0, f"no pin caught the planted mistake {name}"
