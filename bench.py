@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the window + landmark sparse-attention hot path on one MI355X.
+
+One step is one pass over every stage of the path on synthetic inputs that
+are already resident in HBM:
+  1. landmark pooling of K and V (128K-token GQA workload),
+  2. sparse-attention prefill of that workload (64 query / 8 KV heads,
+     d = 128, window 4096, 512 landmarks), O in bf16 and LSE in float32,
+  3. split-KV decode (16 chunks + LSE merge) for 64 sequences with a
+     512K-token bf16 cache (landmarks of the cache pooled once at set-up,
+     timed separately).
+`value` is the prefill's useful TFLOP/s (4*d FLOPs per visible
+(query, key-or-landmark) pair, pooling included in the time); decode is
+reported as algorithmic HBM GB/s alongside.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn fwd TFLOP/s + MFMA util at n=128K; decode HBM GB/s at 512K ctx"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def kernel_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_sparse_msa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name, src_files, per_launch_scale=1.0):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel calibration), if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_hash(*src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def visible_pairs(n, w, G):
+    import numpy as np
+    import long_context_sparse_msa_amd as msa
+
+    win_lo, lm = msa.msa_plan_rows(msa.attn_desc(1, 1, 1, n, 128, w, G))
+    i = np.arange(n, dtype=np.int64)
+    return int((i - win_lo + 1).sum()), int(lm.astype(np.int64).sum())
+
+
+def cpu_baseline(cfg, Q, K, V, rows_per_head, heads):
+    """Time the fp64 oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+    import torch
+
+    import msa_inputs as wl
+    from oracle import msa_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    n, d, w, G = cfg.seq_len, cfg.head_dim, cfg.window, cfg.num_landmarks
+    L = n // G
+    g = heads[0] // (cfg.heads_q // cfg.heads_kv)
+    Kh = K[:, g:g + 1].float().cpu().numpy().astype(np.float64)
+    Vh = V[:, g:g + 1].float().cpu().numpy().astype(np.float64)
+    rows = {h: np.sort(wl.sample_rows(n, h, rows_per_head, w, L)) for h in heads}
+    Qr = {h: Q[:, h].index_select(1, torch.from_numpy(r).to(Q.device)).float().cpu().numpy().astype(np.float64)
+          for h, r in rows.items()}
+    pairs = 0
+    for r in rows.values():
+        pairs += int((np.minimum(r + 1, w)).sum())
+        t = r - w + 1
+        pairs += int(np.clip(np.where(t >= L, t // L, 0), 0, G).sum())
+    t0 = time.perf_counter()
+    Kb = orc.pool(Kh, G)
+    Vb = orc.pool(Vh, G)
+    for h, r in rows.items():
+        Qfull = np.zeros((1, 1, n, d))
+        Qfull[:, 0, r] = Qr[h]
+        orc.attn(Qfull, Kh, Vh, w, G, cfg.scale, rows={0: r}, Kbar=Kb, Vbar=Vb)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * d * pairs
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{cfg.name}: {len(heads)} query heads x {rows_per_head} seeded rows "
+                  f"(+edge rows) of KV head {g}, fp64 numpy, landmark pooling included; "
+                  f"{dt:.1f} s for {flops:.3e} useful FLOPs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle rows per head for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_sparse_msa_amd as msa
+    import msa_inputs as wl
+
+    dev = torch.device("cuda:0")
+    pre, dec = wl.GQA_128K, wl.DECODE_512K
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs, resident in HBM before anything is timed
+    Q, K, V = wl.device_prefill_inputs(pre, dev)
+    B, Hq, Hkv, n, d = pre.batch, pre.heads_q, pre.heads_kv, pre.seq_len, pre.head_dim
+    G = pre.num_landmarks
+    Kb = torch.empty((B, Hkv, G, d), dtype=torch.bfloat16, device=dev)
+    Vb = torch.empty_like(Kb)
+    O = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((B, Hq, n), dtype=torch.float32, device=dev)
+
+    q, Kc, Vc = wl.device_decode_inputs(dec, dev)
+    Kbc = torch.empty((dec.batch, dec.heads_kv, dec.num_landmarks, d), dtype=torch.bfloat16, device=dev)
+    Vbc = torch.empty_like(Kbc)
+    ddesc = msa.decode_desc(dec.batch, dec.heads_q, dec.heads_kv, dec.ctx_len, d, dec.window,
+                            dec.num_landmarks, dec.num_splits)
+    ws = torch.empty(msa.msa_decode_workspace_size(ddesc) // 4, dtype=torch.float32, device=dev)
+    Od = torch.empty((dec.batch, dec.heads_q, d), dtype=torch.bfloat16, device=dev)
+    Ld = torch.empty((dec.batch, dec.heads_q), dtype=torch.float32, device=dev)
+
+    # cache landmarks (static across decode steps): pooled once, timed once
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    msa.msa_pool_landmarks(Kc, Vc, dec.num_landmarks, Kbc, Vbc)
+    e0.record(stream)
+    msa.msa_pool_landmarks(Kc, Vc, dec.num_landmarks, Kbc, Vbc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cache_pool_ms = e0.elapsed_time(e1)
+    cache_bytes = 2 * Kc.numel() * 2 + 2 * Kbc.numel() * 2
+
+    def step(ev):
+        ev[0].record(stream)
+        msa.msa_pool_landmarks(K, V, G, Kb, Vb)
+        ev[1].record(stream)
+        msa.msa_attn_fwd(Q, K, V, Kb, Vb, pre.window, G, pre.scale, O=O, LSE=LSE)
+        ev[2].record(stream)
+        msa.msa_decode_fwd(q, Kc, Vc, Kbc, Vbc, dec.window, dec.num_landmarks, dec.num_splits, dec.scale,
+                           workspace=ws, O=Od, LSE=Ld)
+        ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pool_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    # ---- algorithmic work
+    win_pairs, lm_pairs = visible_pairs(n, pre.window, G)
+    flops = 4.0 * d * (win_pairs + lm_pairs) * Hq * B
+    pool_bytes = 2 * K.numel() * 2 + 2 * Kb.numel() * 2
+    dp = msa.msa_plan_decode(ddesc)
+    entries = dp[2]
+    dec_bytes = (dec.batch * dec.heads_kv * entries * d * 2 * 2      # K and V rows (window + landmarks)
+                 + dec.batch * dec.heads_q * d * 2 * 2               # q in, O out
+                 + dec.batch * dec.heads_q * 4)                      # LSE out
+
+    prefill_tflops = flops / ((pool_ms + attn_ms) * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(prefill_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa_128k prefill (landmark pooling + sparse attention) + decode_512k "
+                        "(split-KV, 16 chunks, LSE merge)",
+            "batch": B, "seq_len": n, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
+            "window": pre.window, "landmarks": G,
+            "decode_batch": dec.batch, "decode_ctx": dec.ctx_len, "decode_splits": dec.num_splits,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel<128, bf16 out>",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles("attn_fwd_gqa_128k", ["attn_bf16.hip", "msa_plan.hpp",
+                                                                   "msa_device.hpp"]),
+            "flops_per_launch": flops,
+            "avg_launch_ms": round(attn_ms, 4),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "ms": round(dec_ms, 4),
+            "roofline": {
+                "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": dec_bytes,
+                "traffic": traffic_from_profiles("decode_512k", ["decode.hip", "msa_plan.hpp",
+                                                                 "msa_device.hpp"]),
+            },
+        },
+        "pool": {
+            "prefill_ms": round(pool_ms, 4),
+            "prefill_GBps": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+            "cache_ms": round(cache_pool_ms, 4),
+            "cache_GBps": round(cache_bytes / (cache_pool_ms * 1e-3) / 1e9, 1),
+        },
+        "kernels_ms": {"pool": round(pool_ms, 4), "attn_fwd": round(attn_ms, 4), "decode": round(dec_ms, 4)},
+        "useful_pairs_per_head": {"window": win_pairs, "landmark": lm_pairs},
+        "cpu_baseline": None,
+    }
+
+    del q, Kc, Vc, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre, Q, K, V, args.cpu_rows, list(range(8)))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

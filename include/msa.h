@@ -1,0 +1,177 @@
+/*
+ * msa.h -- C ABI of libmsa: causal sliding-window + mean-pooled-landmark
+ * sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the fused local-window + landmark ("Flash-MSA") attention
+ * described on the page "Scaling GPU Cluster for Million Token Context",
+ * sections "Why Sparse Attention Changes the Game" (a local window of recent
+ * tokens plus landmark tokens that summarise distant context) and "What is
+ * Flash-MSA Sparse Attention in GPU Clusters?" (one fused, tiled pass that
+ * never writes the score matrix to HBM), made precise as:
+ *
+ *   landmark b   : Kbar_b = mean(K[b*L .. b*L+L-1]),  Vbar_b likewise,
+ *                  L = n / G;
+ *   row i sees   : key j        iff  i - w < j <= i,
+ *                  landmark b   iff  (b+1)*L - 1 <= i - w;
+ *   output       : one softmax over everything row i sees, with scores
+ *                  scale * q_i . k;  O_i = sum p v,
+ *                  LSE_i = m_i + ln(sum exp(s - m_i))   (natural log).
+ *
+ * Decode evaluates the same for the single row i = ctx-1 of a cache, split
+ * into chunks whose partial results are merged by log-sum-exp -- the
+ * single-GPU form of the softmax-statistics aggregation of Ring Attention on
+ * the page "Training at 1M+ Token Context: Ring Attention, YaRN, NTK-Aware
+ * Scaling GPU Cost" (Ring Attention paragraph).
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major, and live in device memory unless stated.
+ *      Q, O      [B][Hq][n][d]      K, V        [B][Hkv][n][d]
+ *      Kbar,Vbar [B][Hkv][G][d]     LSE         [B][Hq][n]   (float32)
+ *      decode q, O [B][Hq][d]       decode LSE  [B][Hq]      (float32)
+ *      caches    [B][Hkv][ctx][d]
+ *    Query head h reads KV head h / (Hq / Hkv).
+ *  - Device pointers must be 16-byte aligned.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no pointer after returning, and holds no state between calls.
+ *  - Compute calls are asynchronous: kernels are enqueued on `stream` (a
+ *    hipStream_t; NULL = the null stream).  Results are valid once the
+ *    caller synchronises that stream.  Calls on different streams that
+ *    write the same buffers race.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is written and nothing is launched.  Error detail is in
+ *    msa_last_error() (thread-local).  A launch failure reported by the HIP
+ *    runtime returns MSA_ERR_HIP.
+ *  - Inputs with NaN or Inf give unspecified results.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment ...      */
+  MSA_ERR_UNSUPPORTED = 2, /* valid but not implemented (head_dim, dtype)    */
+  MSA_ERR_WORKSPACE = 3,   /* decode workspace too small                      */
+  MSA_ERR_HIP = 4,         /* the HIP runtime reported an error               */
+  MSA_ERR_CAPACITY = 5     /* output array of a plan query too small          */
+} msa_status;
+
+typedef enum { MSA_DTYPE_F32 = 0, MSA_DTYPE_BF16 = 1 } msa_dtype;
+
+/* Prefill problem.  head_dim in {64, 128}.  window >= 1 (a window >= n is
+ * plain causal attention).  num_landmarks G >= 0; G > 0 requires n % G == 0.
+ * in_dtype is the dtype of Q, K, V, Kbar, Vbar; out_dtype that of O
+ * (bf16 inputs may write float32 O; float32 inputs write float32 O). */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t window;
+  int32_t num_landmarks;
+  float scale; /* score scale, usually 1/sqrt(head_dim); finite */
+  int32_t in_dtype;  /* msa_dtype */
+  int32_t out_dtype; /* msa_dtype */
+} msa_attn_desc;
+
+/* Decode problem: one new query per sequence at position ctx_len-1, whose
+ * own K/V are already in the cache.  Landmarks are those of the whole cache
+ * (L = ctx_len / G).  num_splits >= 1 chunks of the visible list.  Query
+ * heads per KV head (heads_q / heads_kv) must be <= 16. */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t ctx_len;
+  int32_t head_dim;
+  int32_t window;
+  int32_t num_landmarks;
+  int32_t num_splits;
+  float scale;
+  int32_t in_dtype;
+  int32_t out_dtype;
+} msa_decode_desc;
+
+/* Landmark pooling.  Reads K, V [B][Hkv][n][d] (n = desc->seq_len) and
+ * writes Kbar, Vbar [B][Hkv][G][d]: the mean of each block of L = n/G rows,
+ * accumulated in float32 in a fixed order (deterministic) and rounded to
+ * nearest-even into in_dtype.  Fields read: batch, heads_kv, seq_len,
+ * head_dim, num_landmarks, in_dtype.  G == 0 is a no-op (pointers may be
+ * NULL).  For a decode cache pass an attn desc with seq_len = ctx_len.
+ * Source: the landmark definition above (mean of K and V over each block). */
+msa_status msa_pool_landmarks(const msa_attn_desc* desc, const void* K, const void* V,
+                              void* Kbar, void* Vbar, void* stream);
+
+/* Sparse-attention prefill: O and LSE for every row of every query head.
+ * Kbar/Vbar are the landmarks (from msa_pool_landmarks, or any values of the
+ * same layout); they may be NULL when G == 0.  LSE may be NULL.
+ * Work is enumerated block-sparsely: each workgroup visits only the key
+ * tiles of its rows' windows and the landmark tiles that some row sees.
+ * Source: the operation defined at the top of this file; tiling as in
+ * "What is Flash-MSA Sparse Attention in GPU Clusters?" and the Flash
+ * Attention paragraph of "Training at 1M+ Token Context ...". */
+msa_status msa_attn_fwd(const msa_attn_desc* desc, const void* Q, const void* K, const void* V,
+                        const void* Kbar, const void* Vbar, void* O, float* LSE, void* stream);
+
+/* Bytes of device workspace msa_decode_fwd needs:
+ * num_splits * batch * heads_q * (head_dim + 1) * 4.  Host only. */
+msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes);
+
+/* Decode with split-KV partial softmax and an LSE merge.
+ * The ordered visible list of row ctx-1 (visible landmarks in block order,
+ * then the window keys ascending; E entries) is cut into num_splits chunks
+ * of s = ceil(E / num_splits) entries; chunk c covers [c*s, min(E,(c+1)*s)).
+ * Pass 1 writes each chunk's normalised output and log-sum-exp into the
+ * workspace: o_c float32 [S][B][Hq][d] at offset 0, then lse_c float32
+ * [S][B][Hq] (an empty chunk has lse_c = -inf, o_c = 0).  Pass 2 merges:
+ * LSE = ln sum_c exp(lse_c), O = sum_c exp(lse_c - LSE) o_c.
+ * The workspace is caller-owned scratch of at least
+ * msa_decode_workspace_size() bytes; its contents after the call are the
+ * partials described above.  Kbar/Vbar: landmarks of the caches (NULL if
+ * G == 0).  LSE may be NULL.  in_dtype must be bf16 or f32. */
+msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void* Kcache,
+                          const void* Vcache, const void* Kbar, const void* Vbar, void* workspace,
+                          size_t workspace_bytes, void* O, float* LSE, void* stream);
+
+/* ---- Host-only introspection: the exact schedule the kernels use.  These
+ * make no HIP call and need no GPU; all pointers are host memory. ---- */
+
+/* Per row i in [0, n): win_lo[i] = lowest visible window key, lm_count[i] =
+ * number of visible landmarks (they are always landmarks 0..lm_count-1). */
+msa_status msa_plan_rows(const msa_attn_desc* desc, int32_t* win_lo, int32_t* lm_count);
+
+/* The tiles msa_attn_fwd visits, in kernel order, as int32 quadruples
+ * (query_tile, kind, tile, interior): kind 0 = landmark tile (landmarks
+ * tile*bn .. tile*bn+bn-1), 1 = window key tile (keys tile*bn ..);
+ * interior = 1 when every (row, key) of the tile is visible so the kernel
+ * applies no mask.  Query tile t covers rows t*bm .. min(n, t*bm+bm)-1.
+ * Writes *count (always) and *bm, *bn; writes `out` only if capacity >=
+ * *count (else MSA_ERR_CAPACITY); out may be NULL to query the count. */
+msa_status msa_plan_tiles(const msa_attn_desc* desc, int32_t* out, int64_t capacity,
+                          int64_t* count, int32_t* bm, int32_t* bn);
+
+/* Decode schedule: chunk_bounds[0..num_splits] (entry offsets of the
+ * chunks), *lm_visible = visible landmarks of row ctx-1, *entries = E. */
+msa_status msa_plan_decode(const msa_decode_desc* desc, int32_t* chunk_bounds,
+                           int32_t* lm_visible, int32_t* entries);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* msa_last_error(void);
+/* MSA_ABI_VERSION of the loaded library. */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

@@ -1,0 +1,29 @@
+"""MI355X-native causal sliding-window + mean-pooled-landmark sparse attention.
+
+The compute lives in libmsa.so (C ABI in include/msa.h, gfx950 HIP kernels
+under csrc/); this package is its thin Python binding.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    MSA_DTYPE_BF16,
+    MSA_DTYPE_F32,
+    AttnDesc,
+    DecodeDesc,
+    MsaError,
+    abi_version,
+    attn_desc,
+    decode_desc,
+    decode_partials,
+    lib,
+    msa_attn_fwd,
+    msa_decode_fwd,
+    msa_decode_workspace_size,
+    msa_plan_decode,
+    msa_plan_rows,
+    msa_plan_tiles,
+    msa_pool_landmarks,
+)
+
+pool_landmarks = msa_pool_landmarks
+attn_fwd = msa_attn_fwd
+decode_fwd = msa_decode_fwd

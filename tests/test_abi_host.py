@@ -1,0 +1,195 @@
+"""Host-side tests of libmsa's C ABI: the library loads and exports every
+symbol the header declares, validation rejects bad arguments before any
+launch, and the schedule it reports is bit-exact against the oracle's
+mask-derived plans.  No GPU is used (only host-only exports and calls that
+fail validation)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import msa_inputs as wl
+from oracle import msa_oracle as orc
+
+msa = pytest.importorskip("long_context_sparse_msa_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return msa.lib()
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "msa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) == 10
+    assert sorted(msa.EXPORTS) == names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    assert msa.abi_version() == 1
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.msa_status_string(s)
+    assert L.msa_status_string(99) == b"unknown status"
+
+
+def call_attn(desc, ptr=16):
+    p = ctypes.c_void_p(ptr)
+    return msa.lib().msa_attn_fwd(ctypes.byref(desc), p, p, p, p, p, p, None, None)
+
+
+def base_desc(**kw):
+    args = dict(batch=1, heads_q=4, heads_kv=2, seq_len=256, head_dim=128, window=64, num_landmarks=4,
+                scale=0.1, in_dtype=msa.MSA_DTYPE_BF16, out_dtype=msa.MSA_DTYPE_BF16)
+    args.update(kw)
+    return msa.AttnDesc(*[args[k] for k, _ in msa.AttnDesc._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), 1), (dict(window=-3), 1), (dict(num_landmarks=-1), 1), (dict(num_landmarks=3), 1),
+    (dict(heads_q=3), 1), (dict(heads_kv=0), 1), (dict(head_dim=96), 2), (dict(head_dim=256), 2),
+    (dict(in_dtype=7), 1), (dict(out_dtype=5), 1), (dict(batch=-1), 1), (dict(seq_len=-5), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(in_dtype=msa.MSA_DTYPE_F32, out_dtype=msa.MSA_DTYPE_BF16), 2),
+])
+def test_attn_validation(kw, status):
+    assert call_attn(base_desc(**kw)) == status
+    assert msa.lib().msa_last_error()
+
+
+def test_attn_null_and_misaligned_pointers():
+    L = msa.lib()
+    d = base_desc()
+    p = ctypes.c_void_p(16)
+    assert L.msa_attn_fwd(ctypes.byref(d), None, p, p, p, p, p, None, None) == 1
+    assert b"Q is NULL" in L.msa_last_error()
+    assert L.msa_attn_fwd(ctypes.byref(d), p, p, p, ctypes.c_void_p(24), p, p, None, None) == 1
+    assert b"Kbar is not 16-byte aligned" in L.msa_last_error()
+    # no landmarks: Kbar/Vbar may be NULL; an empty problem launches nothing
+    d0 = base_desc(num_landmarks=0, batch=0)
+    assert L.msa_attn_fwd(ctypes.byref(d0), p, p, p, None, None, p, None, None) == 0
+
+
+def test_python_binding_raises():
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_plan_rows(base_desc(window=0))
+    assert e.value.status == 1
+
+
+def dec_desc(**kw):
+    args = dict(batch=2, heads_q=8, heads_kv=2, ctx_len=512, head_dim=128, window=64, num_landmarks=8,
+                num_splits=4, scale=0.1, in_dtype=msa.MSA_DTYPE_BF16, out_dtype=msa.MSA_DTYPE_BF16)
+    args.update(kw)
+    return msa.DecodeDesc(*[args[k] for k, _ in msa.DecodeDesc._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_splits=0), 1), (dict(window=0), 1), (dict(num_landmarks=7), 1), (dict(ctx_len=0), 1),
+    (dict(heads_q=6, heads_kv=4), 1), (dict(heads_q=64, heads_kv=2), 2), (dict(head_dim=32), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32), 2),
+])
+def test_decode_validation(kw, status):
+    d = dec_desc(**kw)
+    p = ctypes.c_void_p(16)
+    assert msa.lib().msa_decode_fwd(ctypes.byref(d), p, p, p, p, p, p, 1 << 30, p, None, None) == status
+
+
+def test_decode_workspace_checks():
+    d = dec_desc()
+    need = msa.msa_decode_workspace_size(d)
+    assert need == 4 * 2 * 8 * 129 * 4
+    p = ctypes.c_void_p(16)
+    assert msa.lib().msa_decode_fwd(ctypes.byref(d), p, p, p, p, p, p, need - 4, p, None, None) == 3
+    assert b"workspace" in msa.lib().msa_last_error()
+
+
+def test_pool_validation():
+    L = msa.lib()
+    p = ctypes.c_void_p(16)
+    d = base_desc(num_landmarks=3)
+    assert L.msa_pool_landmarks(ctypes.byref(d), p, p, p, p, None) == 1
+    d = base_desc(num_landmarks=0)
+    assert L.msa_pool_landmarks(ctypes.byref(d), None, None, None, None, None) == 0
+
+
+# ------------------------------------------------------------------ plans
+
+SHAPES = [
+    # (n, w, G) -- the workload shapes, then ragged and degenerate ones
+    (2048, 256, 16), (32768, 4096, 512), (131072, 4096, 512),
+    (64, 1, 0), (64, 64, 64), (192, 50, 3), (320, 1000, 5), (130, 7, 0), (1, 1, 0), (1, 1, 1),
+    (100, 3, 10), (4096, 128, 4096), (777, 100, 7), (65, 65, 13),
+]
+
+
+@pytest.mark.parametrize("n,w,G", SHAPES + [(1048576, 4096, 512)])
+@pytest.mark.parametrize("dtype", [msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_F32])
+def test_plan_rows_bitexact(n, w, G, dtype):
+    d = base_desc(seq_len=n, window=w, num_landmarks=G, in_dtype=dtype, out_dtype=dtype)
+    win_lo, lm = msa.msa_plan_rows(d)
+    if n > 200000:
+        rows = np.unique(np.concatenate([np.arange(0, 3 * w), np.random.default_rng(0).choice(n, 20000),
+                                         np.arange(n - 2 * w, n)]))
+    else:
+        rows = np.arange(n)
+    o_lo, o_lm = orc.row_plan(n, w, G, rows)
+    np.testing.assert_array_equal(win_lo[rows], o_lo)
+    np.testing.assert_array_equal(lm[rows], o_lm)
+
+
+@pytest.mark.parametrize("n,w,G", SHAPES + [(1048576, 4096, 512)])
+@pytest.mark.parametrize("dtype", [msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_F32])
+def test_plan_tiles_bitexact(n, w, G, dtype):
+    d = base_desc(seq_len=n, window=w, num_landmarks=G, in_dtype=dtype, out_dtype=dtype)
+    tiles, bm, bn = msa.msa_plan_tiles(d)
+    T = -(-n // bm)
+    if T > 300:
+        rng = np.random.default_rng(1)
+        qt = sorted(set(range(0, 40)) | set(range(T - 8, T)) | set(rng.choice(T, 60, replace=False).tolist()))
+    else:
+        qt = list(range(T))
+    want = orc.tile_plan(n, w, G, bm, bn, q_tiles=qt)
+    sel = np.isin(tiles[:, 0], qt)
+    got = [tuple(int(x) for x in r[:3]) + (bool(r[3]),) for r in tiles[sel]]
+    assert got == want
+    # every query tile appears (each row sees at least itself)
+    assert set(tiles[:, 0].tolist()) == set(range(T))
+
+
+def test_plan_tile_counts_workloads():
+    # Visible-tile totals per head for the 128K and 1M workloads: the
+    # window part is w/bn + bm/bn (+1 for a straddling start) tiles per
+    # query tile once past the ramp.
+    for cfg in (wl.GQA_128K, wl.GQA_1M):
+        d = base_desc(seq_len=cfg.seq_len, window=cfg.window, num_landmarks=cfg.num_landmarks)
+        tiles, bm, bn = msa.msa_plan_tiles(d)
+        win = tiles[tiles[:, 1] == 1]
+        per_t = np.bincount(win[:, 0])
+        T = cfg.seq_len // bm
+        assert per_t[cfg.window // bm:].max() == cfg.window // bn + bm // bn
+        assert per_t.sum() <= T * (cfg.window // bn + bm // bn)
+
+
+@pytest.mark.parametrize("ctx,w,G,S", [(524288, 4096, 512, 16), (512, 64, 8, 4), (100, 1000, 0, 3),
+                                        (64, 8, 8, 40), (4096, 300, 16, 7), (1, 1, 1, 2)])
+def test_plan_decode_bitexact(ctx, w, G, S):
+    d = dec_desc(ctx_len=ctx, window=w, num_landmarks=G, num_splits=S)
+    bounds, lm, ent = msa.msa_plan_decode(d)
+    kinds, idx = orc.visible_list(ctx - 1, ctx, w, G)
+    assert ent == len(idx)
+    assert lm == int((kinds == 0).sum())
+    np.testing.assert_array_equal(bounds, orc.chunk_bounds(len(idx), S))
