@@ -54,6 +54,54 @@ def traffic_from_profiles(name, src_files, per_launch_scale=1.0):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
+def _pmc_rows(path, counter):
+    import csv
+
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out[r["Dispatch_Id"]] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per launch of the prefill and decode kernels from a
+    rocprofv3 --pmc run of this bench with --calibrate-copy.  Each counter
+    (KiB per dispatch) is scaled by what it reads for the 1 GiB copy."""
+    fetch = _pmc_rows(fetch_csv, "FETCH_SIZE")
+    write = _pmc_rows(write_csv, "WRITE_SIZE")
+
+    def calib(rows):
+        copies = [v for (name, v) in rows.values() if "copyBuffer" in name]
+        return COPY_BYTES / (max(copies) * 1024.0)
+
+    fs, ws = calib(fetch), calib(write)
+    out = {}
+    for key, needle, srcs in (("attn_fwd_gqa_128k", "attn_fwd_bf16_kernel",
+                               ["attn_bf16.hip", "msa_plan.hpp", "msa_device.hpp"]),
+                              ("decode_512k", "decode_split_kernel", ["decode.hip", "msa_plan.hpp", "msa_device.hpp"])):
+        fv = [v for (name, v) in fetch.values() if needle in name]
+        wv = [v for (name, v) in write.values() if needle in name]
+        if key.startswith("decode"):
+            fv += [v for (name, v) in fetch.values() if "decode_merge_kernel" in name][: len(fv)]
+            wv += [v for (name, v) in write.values() if "decode_merge_kernel" in name][: len(wv)]
+            nl = max(1, len([1 for (name, _) in fetch.values() if needle in name]))
+        else:
+            nl = max(1, len(fv))
+        fb = sum(fv) * 1024.0 * fs / nl
+        wb = sum(wv) * 1024.0 * ws / max(1, len([1 for (name, _) in write.values() if needle in name]))
+        rec = {"source_hash": kernel_hash(*srcs), "fetch_bytes": fb, "write_bytes": wb,
+               "bytes_per_launch": fb + wb, "fetch_scale": fs, "write_scale": ws, "launches": nl}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        out[key] = rec
+    print(json.dumps(out, indent=1))
+
+
 def visible_pairs(n, w, G):
     import numpy as np
     import long_context_sparse_msa_amd as msa
@@ -115,8 +163,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle rows per head for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=49152, help="oracle rows per head for the CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB device-to-device copy before timing (reference dispatch for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run into "
+                         "profiles/traffic_*.json and print the summary; runs nothing on the GPU")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
@@ -130,6 +186,12 @@ def main():
     dev = torch.device("cuda:0")
     pre, dec = wl.GQA_128K, wl.DECODE_512K
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        x = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
 
     # ---- inputs, resident in HBM before anything is timed
     Q, K, V = wl.device_prefill_inputs(pre, dev)

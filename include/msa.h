@@ -78,7 +78,7 @@ typedef struct {
   int32_t head_dim;
   int32_t window;
   int32_t num_landmarks;
-  float scale; /* score scale, usually 1/sqrt(head_dim); finite */
+  float scale; /* score scale, usually 1/sqrt(head_dim); finite and > 0 */
   int32_t in_dtype;  /* msa_dtype */
   int32_t out_dtype; /* msa_dtype */
 } msa_attn_desc;
@@ -96,7 +96,7 @@ typedef struct {
   int32_t window;
   int32_t num_landmarks;
   int32_t num_splits;
-  float scale;
+  float scale; /* finite and > 0 */
   int32_t in_dtype;
   int32_t out_dtype;
 } msa_decode_desc;

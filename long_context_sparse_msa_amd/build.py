@@ -42,9 +42,16 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  The prefill kernel never relies on NaN semantics
+# (NaN inputs give unspecified results), and without IEEE NaN handling the
+# compiler drops the canonicalising max it otherwise puts in front of every
+# max of an MFMA result.
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in ln]

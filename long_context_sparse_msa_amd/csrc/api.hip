@@ -71,7 +71,8 @@ msa_status check_attn(const msa_attn_desc* d) {
   if (s != MSA_OK) return s;
   if (d->window < 1) return fail(MSA_ERR_INVALID_ARG, "window=%d must be >= 1", d->window);
   if (d->window > (1 << 30)) return fail(MSA_ERR_INVALID_ARG, "window=%d too large (max 2^30)", d->window);
-  if (!isfinite(d->scale)) return fail(MSA_ERR_INVALID_ARG, "scale is not finite");
+  if (!isfinite(d->scale) || !(d->scale > 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (d->out_dtype != MSA_DTYPE_F32 && d->out_dtype != MSA_DTYPE_BF16)
     return fail(MSA_ERR_INVALID_ARG, "out_dtype=%d is not a msa_dtype", d->out_dtype);
   if (d->in_dtype == MSA_DTYPE_F32 && d->out_dtype != MSA_DTYPE_F32)
@@ -97,7 +98,8 @@ msa_status check_decode(const msa_decode_desc* d) {
     return fail(MSA_ERR_INVALID_ARG, "num_landmarks=%d must be >= 0 and divide ctx_len=%d", d->num_landmarks,
                 d->ctx_len);
   if (d->num_splits < 1) return fail(MSA_ERR_INVALID_ARG, "num_splits=%d must be >= 1", d->num_splits);
-  if (!isfinite(d->scale)) return fail(MSA_ERR_INVALID_ARG, "scale is not finite");
+  if (!isfinite(d->scale) || !(d->scale > 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (d->in_dtype != MSA_DTYPE_BF16)
     return fail(MSA_ERR_UNSUPPORTED, "decode reads bf16 caches only (in_dtype=%d)", d->in_dtype);
   if (d->out_dtype != MSA_DTYPE_F32 && d->out_dtype != MSA_DTYPE_BF16)

@@ -8,22 +8,33 @@
 // Clusters?": one fused pass, tiles kept on chip, scores never written out).
 //
 // How, on CDNA4:
-//  * A workgroup owns BM = 128 query rows of one head (4 wavefronts x 32
-//    rows) and walks only the key tiles that matter: the landmark tiles
+//  * A query tile is BM = 128 rows of one head (4 wavefronts x 32 rows).
+//    Its walk visits only the key tiles that matter: the landmark tiles
 //    0 .. ceil(c(r_last)/64)-1, then the window tiles covering
 //    [r_first-w+1, r_last] (closed forms in msa_plan.hpp).  Masks are
 //    evaluated only on edge tiles.
-//  * Both contractions run on v_mfma_f32_16x16x32_bf16.  Scores are formed
-//    transposed, S^T = K Q^T, so that each lane's accumulator holds 16 keys
-//    of one query row -- exactly the B operand layout of O^T = V^T P^T.  P
-//    therefore never leaves registers, the row max/sum need only two
-//    cross-lane steps, and the per-row rescale of O is a per-lane scalar.
-//  * K tiles are staged row-major and V tiles transposed in LDS (padded
-//    strides keep both the staging writes and the operand reads free of
-//    bank conflicts), double-buffered with one barrier per tile; the next
-//    tile's global loads are in flight while the current one is computed.
-//  * The online softmax works in base 2 with scale*log2(e) folded into the
-//    fp32 scores.
+//  * Both contractions run on v_mfma_f32_32x32x16_bf16.  Scores are formed
+//    transposed, S^T = K Q^T, so each lane's accumulator holds 16 keys of
+//    one query row -- the B-operand layout of O^T += V^T P^T.  P never
+//    leaves registers; a row's max and sum need one lane-half swap
+//    (v_permlane32_swap); the rescale of O is a per-lane scalar.
+//  * Softmax in base 2 with scale*log2(e) folded into one FMA per score,
+//    raw v_exp_f32, packed bf16 converts.  O is normalised by the bf16 dot2
+//    sum of the packed P (exactly the P that multiplies V, so a dominant key
+//    gives O = its value), LSE by a float32 sum of P.  The running max is
+//    raised only when a tile's max exceeds it by more than 2^8 in
+//    probability; until then P stays bounded by 256 and O and the sums are
+//    not rescaled -- exact, since they share the same reference.
+//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//    destination; no registers, no vector ALU work), row-major with 16-byte
+//    chunks XOR-swizzled by row.  K operands are row-per-lane 16-byte reads;
+//    V^T operands come from row-major V through the CDNA4 transpose read
+//    ds_read_b64_tr_b16.  Both swizzles make those reads conflict-free.
+//    The buffer range check skips rows past the end; those LDS rows keep
+//    finite earlier contents and are masked.
+//  * A workgroup is 4 wavefronts with double-buffered K/V tiles and one
+//    barrier per tile; two workgroups share a CU, so each SIMD runs two
+//    wavefronts whose matrix-core and vector-ALU work interleave.
 //  * Workgroups are renumbered XCD-aware: each XCD sweeps one KV head's
 //    query tiles from the last (heaviest) to the first, all query heads of
 //    the group back to back, so K/V tiles are shared in that XCD's L2.
@@ -37,325 +48,433 @@ namespace {
 constexpr int BM = kBM_BF16;  // 128
 constexpr int BN = kBN_BF16;  // 64
 constexpr int kThreads = 256;
+constexpr float kRescaleTh = 8.0f;  // log2 of the largest unnormalised P
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records in bytes, 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// (x[l], x[l^32]) for every lane l, as a pair whose max or sum is the
+// value over both halves of the wavefront.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles: 64 rows (keys) x D bf16, row-major, 16-byte chunks permuted
+// within a row.  K: chunk c of row r sits at slot c ^ (r mod CH), so the 16
+// rows a K-operand read touches at once land on 16 distinct slots.  V:
+// chunk c of row r sits at slot c ^ ((r mod 4) * CH/4), so the 4 rows x 4
+// chunks a transpose read touches land on 16 distinct slots.
 template <int D>
-struct Lds {
-  static constexpr int KS = D + 8;   // K row stride (elements): 16-byte pad
-  static constexpr int VS = BN + 4;  // V^T row stride (elements): 8-byte pad
-  static constexpr int kTile = BN * KS;
-  static constexpr int vTile = D * VS;
-  static constexpr int kBuf = kTile + vTile;  // one buffer (elements)
+struct Smem {
+  static constexpr int RB = D * 2;      // bytes per row
+  static constexpr int CH = RB / 16;    // 16-byte chunks per row
+  static constexpr int TILE = BN * RB;  // bytes per tile
+  static constexpr int BYTES = 4 * TILE;
+  __device__ static constexpr int kbuf(int i) { return i * TILE; }
+  __device__ static constexpr int vbuf(int i) { return (2 + i) * TILE; }
+  __device__ static constexpr int kswz(int r) { return r % CH; }
+  __device__ static constexpr int vswz(int r) { return (r % 4) * (CH / 4); }
 };
 
-// Global -> register staging of one K/V tile (64 keys x D).
+// Issues the direct-to-LDS loads of one 64-key tile for the threads of a
+// 256-thread group: instruction i of wavefront wv fills LDS bytes
+// [i*4096 + wv*1024, +1024) of the tile, lane l the 16 bytes at l*16.
 template <int D>
-struct TileLoader {
-  static constexpr int kChunksK = BN * D / 8 / kThreads;      // 16-byte chunks of K per thread
-  static constexpr int kVItems = 16 * (D / 8);                 // (4-key group, 8-dim group) items
-  u32x4 kreg[kChunksK];
-  u32x4 vreg[4];
+struct Stager {
+  using SM = Smem<D>;
+  static constexpr int kInsts = SM::TILE / (kThreads * 16);  // 4 (D=128), 2 (D=64)
+  uint32_t koff[kInsts];  // global byte offsets within a tile, K swizzle
+  uint32_t voff[kInsts];  // same, V swizzle
+  int wv;
 
-  // rows [row0, row0+64) of src (clamped to valid-1; clamped rows are masked)
-  __device__ void load(const uint16_t* __restrict__ Ksrc, const uint16_t* __restrict__ Vsrc,
-                       int row0, int valid, int tid) {
+  __device__ void init(int gtid) {
+    wv = gtid >> 6;
+    const int lane = gtid & 63;
 #pragma unroll
-    for (int c = 0; c < kChunksK; ++c) {
-      const int idx = tid + c * kThreads;
-      const int r = idx / (D / 8);
-      const int col = idx % (D / 8);
-      int row = row0 + r;
-      row = row < valid ? row : valid - 1;
-      kreg[c] = *reinterpret_cast<const u32x4*>(Ksrc + (size_t)row * D + col * 8);
+    for (int i = 0; i < kInsts; ++i) {
+      const int q = (i * 4 + wv) * 64 + lane;  // 16-byte slot index within the tile
+      const int r = q / SM::CH;
+      const int slot = q % SM::CH;
+      koff[i] = (uint32_t)(r * SM::RB + ((slot ^ SM::kswz(r)) * 16));
+      voff[i] = (uint32_t)(r * SM::RB + ((slot ^ SM::vswz(r)) * 16));
     }
-    if (tid < kVItems) {
-      const int kg = tid % 16;
-      const int dg = tid / 16;
+  }
+  __device__ void issue(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* off, unsigned char* tile, int row0) const {
+    const uint32_t soff = (uint32_t)row0 * SM::RB;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int row = row0 + kg * 4 + r;
-        row = row < valid ? row : valid - 1;
-        vreg[r] = *reinterpret_cast<const u32x4*>(Vsrc + (size_t)row * D + dg * 8);
+    for (int i = 0; i < kInsts; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(tile + i * 4096 + wv * 1024), 16, off[i], soff,
+                                               0, 0);
+    }
+  }
+  __device__ void issue_k(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int row0) const {
+    issue(r, koff, tile, row0);
+  }
+  __device__ void issue_v(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int row0) const {
+    issue(r, voff, tile, row0);
+  }
+};
+
+// Per-lane LDS offsets of the MFMA operands within a tile.
+//  K operand of S^T = K Q^T, k-step ks, 32-key block mb: row mb*32 + r32,
+//    dims ks*16 + g2*8 .. +7 (one 16-byte read).
+//  V^T operand of O^T += V^T P^T, 16-key step kk, 32-dim block db: two
+//    transpose reads of 4 keys x 4 dims per lane; within each 16-lane group
+//    lane j points at key (base + j/4), dims (dbase + 4*(j%4)); the read
+//    hands lane j the 4 keys of dim dbase + j.
+template <int D>
+struct Frag {
+  using SM = Smem<D>;
+  uint32_t k[D / 16];  // per ks (mb adds 32 rows)
+  uint32_t v[D / 32];  // per db (kk adds 16 rows, the second read 8 rows)
+
+  __device__ void init(int lane) {
+    const int r32 = lane & 31, g2 = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int c = ks * 2 + g2;
+      k[ks] = (uint32_t)(r32 * SM::RB + ((c ^ SM::kswz(r32)) * 16));
+    }
+    const int g = lane >> 4, j = lane & 15;
+    const int key = (g >> 1) * 4 + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + (g & 1) * 16 + 4 * (j & 3);
+      const int c = d / 8;
+      v[db] = (uint32_t)(key * SM::RB + ((c ^ SM::vswz(key)) * 16) + (d % 8) * 2);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Per-lane running state of one query row (shared with the lane l^32).
+template <int D>
+struct RowState {
+  f32x16 o[D / 32];  // O^T accumulators: o[db][jj*4+i] = dim db*32 + jj*8 + g2*4 + i
+  float m;           // running reference max (base-2 units)
+  float l;           // this lane's share of sum(bf16 P): normalises O
+  float ls;          // this lane's share of sum(P) in float32: gives LSE
+};
+
+// Which keys of a tile a wavefront's rows [wr0, wr1] see: visit the tile at
+// all (any) and apply no mask (interior).
+struct TileVis {
+  bool any, interior;
+};
+
+__device__ __forceinline__ TileVis tile_vis(bool is_lm, int key0, int wr0, int wr1, int wlm_lo, int wlm_hi,
+                                            int w) {
+  TileVis v;
+  if (is_lm) {
+    v.any = key0 < wlm_hi;
+    v.interior = key0 + BN <= wlm_lo;
+  } else {
+    v.any = key0 <= wr1 && key0 + BN - 1 >= wr0 - w + 1;
+    v.interior = key0 + BN - 1 <= wr0 && key0 >= wr1 - w + 1;
+  }
+  return v;
+}
+
+// -inf on every score this lane's row does not see.
+__device__ __forceinline__ void mask_tile(f32x16* s, bool is_lm, int key0, int row, int lmc, int w, int g2) {
+  const int base = row - key0 - g2 * 4;  // row - key = base - (mb*32 + jj*8 + i)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int off = mb * 32 + jj * 8 + i;
+        const bool vis = is_lm ? (key0 + g2 * 4 + off < lmc) : ((unsigned)(base - off) < (unsigned)w);
+        s[mb][jj * 4 + i] = vis ? s[mb][jj * 4 + i] : -INFINITY;
       }
     }
   }
+}
 
-  __device__ void store(uint16_t* __restrict__ buf, int tid) const {
-    using L = Lds<D>;
+// Online softmax of one tile's scores: raises the reference max when the
+// tile exceeds it by more than 2^kRescaleTh (rescaling O and the sums), then
+// forms P = exp2(s*c2 - m) packed to bf16 as the B operand of O^T += V^T P^T.
+// Slots g2*8+0..3 <-> keys kk*16+g2*4+0..3, g2*8+4..7 <-> keys kk*16+8+g2*4+0..3.
+template <int D>
+__device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState<D>& st, bf16x8* pf) {
+  float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < kChunksK; ++c) {
-      const int idx = tid + c * kThreads;
-      const int r = idx / (D / 8);
-      const int col = idx % (D / 8);
-      *reinterpret_cast<u32x4*>(buf + r * L::KS + col * 8) = kreg[c];
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[mb][e], s[mb][e + 1]));
+  }
+  mx = half_max(mx) * c2;
+  if (__any(mx > st.m + kRescaleTh)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+    st.ls *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+  }
+  const float nm = -st.m;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int mb = kk >> 1;
+    const int j0 = (kk & 1) * 2;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j0 * 4 + i], c2, nm));
+      p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][(j0 + 1) * 4 + i], c2, nm));
     }
-    if (tid < kVItems) {
-      const int kg = tid % 16;
-      const int dg = tid / 16;
-      uint16_t* vt = buf + L::kTile;
-      // 4 keys x 8 dims in registers -> 8 rows of V^T, 4 keys each.
+    st.ls += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    // Packed words are kept as separate scalars: feeding the dot2 builtin
+    // with elements of a vector under construction is miscompiled by this
+    // toolchain (every dot2 then reads element 0).
+    const uint32_t w0 = cvt_pk(p[0], p[1]);
+    const uint32_t w1 = cvt_pk(p[2], p[3]);
+    const uint32_t w2 = cvt_pk(p[4], p[5]);
+    const uint32_t w3 = cvt_pk(p[6], p[7]);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, st.l, false);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, st.l, false);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, st.l, false);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, st.l, false);
+    pf[kk] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+  }
+}
+
+// The matrix-core work of one step: optionally O^T += V^T P^T for one tile
+// (PV) and S^T = K Q^T for another (QK), as one unrolled stream of operand
+// fragments read from LDS a fixed window ahead of the MFMA consuming them.
+// Consecutive MFMAs use independent accumulators.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigned char* kt, const Frag<D>& fr,
+                                          const bf16x8* qf, const bf16x8* pf, f32x16* o, f32x16* s) {
+  using SM = Smem<D>;
+  constexpr int DB = D / 32;
+  constexpr int KS = D / 16;
+  constexpr int NPV = PV ? 4 * DB : 0;  // (kk, db), db fastest
+  constexpr int NQK = QK ? 2 * KS : 0;  // (ks, mb), mb fastest
+  constexpr int N = NPV + NQK;
+  constexpr int W = 6;                  // fragments in flight
+  u32x4 f[N];
+  auto load = [&](int i) -> u32x4 {
+    if (i < NPV) {
+      const int kk = i / DB, db = i % DB;
+      const unsigned char* p = vt + fr.v[db] + kk * 16 * SM::RB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p + 8 * SM::RB));
+      const auto a = __builtin_bit_cast(u32x2, lo);
+      const auto c = __builtin_bit_cast(u32x2, hi);
+      return u32x4{a[0], a[1], c[0], c[1]};
+    }
+    const int q = i - NPV;
+    const int ks = q / 2, mb = q % 2;
+    return *reinterpret_cast<const u32x4*>(kt + fr.k[ks] + mb * 32 * SM::RB);
+  };
+  if constexpr (QK) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t a = (vreg[0][word] >> sh) & 0xffffu;
-        const uint32_t b = (vreg[1][word] >> sh) & 0xffffu;
-        const uint32_t c = (vreg[2][word] >> sh) & 0xffffu;
-        const uint32_t d = (vreg[3][word] >> sh) & 0xffffu;
-        u32x2 pk;
-        pk[0] = a | (b << 16);
-        pk[1] = c | (d << 16);
-        *reinterpret_cast<u32x2*>(vt + (dg * 8 + e) * L::VS + kg * 4) = pk;
+  for (int i = 0; i < W && i < N; ++i) f[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + W < N) f[i + W] = load(i + W);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, f[i]);
+    if (i < NPV) {
+      const int kk = i / DB, db = i % DB;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[db], 0, 0, 0);
+    } else {
+      const int q = i - NPV;
+      const int ks = q / 2, mb = q % 2;
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+    }
+  }
+}
+
+// O = O_acc / sum(bf16 P), LSE = (m + log2 sum(P)) ln 2.
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void store_rows(const RowState<D>& st, int row, int n, int g2, size_t q_off,
+                                           size_t lse_off, void* __restrict__ Out, float* __restrict__ LSE) {
+  const float lt = half_sum(st.l);
+  const float lst = half_sum(st.ls);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (row >= n) return;
+  const size_t base = q_off + (size_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dcol = db * 32 + jj * 8 + g2 * 4;
+      const float v0 = st.o[db][jj * 4 + 0] * inv, v1 = st.o[db][jj * 4 + 1] * inv;
+      const float v2 = st.o[db][jj * 4 + 2] * inv, v3 = st.o[db][jj * 4 + 3] * inv;
+      if constexpr (OUT_BF16) {
+        const u32x2 pk = {cvt_pk(v0, v1), cvt_pk(v2, v3)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + base + dcol) = pk;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + base + dcol) = f32x4{v0, v1, v2, v3};
       }
     }
   }
+  if (LSE != nullptr && g2 == 0) LSE[lse_off + row] = (st.m + log2f(lst)) * kLn2;
+}
+
+// Everything a workgroup needs to walk the tiles of one query tile.
+template <int D>
+struct Walk {
+  TileRange tr;
+  int n_tiles;
+  __amdgpu_buffer_rsrc_t rk, rv, rkl, rvl;  // window and landmark K/V of the KV head
+  int n;
+
+  __device__ void init(const uint16_t* K, const uint16_t* V, const uint16_t* Kb, const uint16_t* Vb, int b,
+                       int Hkv, int kvh, int t, int n_, int w, int G, int L) {
+    n = n_;
+    tr = tile_range(t, BM, BN, n, w, G, L);
+    n_tiles = tr.n_lm_tiles + (tr.kt_hi - tr.kt_lo + 1);
+    const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)n * D;
+    rk = make_rsrc(K + kv_off, (uint32_t)n * D * 2u);
+    rv = make_rsrc(V + kv_off, (uint32_t)n * D * 2u);
+    rkl = rk;
+    rvl = rv;
+    if (G > 0) {
+      const size_t lm_off = ((size_t)b * Hkv + kvh) * (size_t)G * D;
+      rkl = make_rsrc(Kb + lm_off, (uint32_t)G * D * 2u);
+      rvl = make_rsrc(Vb + lm_off, (uint32_t)G * D * 2u);
+    }
+  }
+  __device__ bool is_lm(int it) const { return it < tr.n_lm_tiles; }
+  // First key (landmark index or position) of tile it.  Past the last tile:
+  // n, beyond the window buffer, so loads of it are range-checked away and
+  // touch no memory.
+  __device__ int key0(int it) const {
+    return it >= n_tiles ? n : (it < tr.n_lm_tiles ? it * BN : (tr.kt_lo + it - tr.n_lm_tiles) * BN);
+  }
+  __device__ __amdgpu_buffer_rsrc_t ksrc(int it) const { return is_lm(it) ? rkl : rk; }
+  __device__ __amdgpu_buffer_rsrc_t vsrc(int it) const { return is_lm(it) ? rvl : rv; }
 };
 
-__device__ __forceinline__ float wave_max16(float x) {
-  // max over the 4 lanes that share (lane mod 16)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Q fragments of one row (B operand of S^T = K Q^T).
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, size_t q_off, int row, int n, int g2,
+                                       bf16x8* qf) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < n) v = *reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row * D + ks * 16 + g2 * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
 }
 
-__device__ __forceinline__ float wave_sum16(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Zero the tile buffers once: rows the range check skips keep finite values.
+template <int D>
+__device__ __forceinline__ void zero_smem(unsigned char* smem, int tid, int nthreads) {
+  for (int i = tid; i < Smem<D>::BYTES / 16; i += nthreads) {
+    reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
+// Wait for this wavefront's direct-to-LDS loads, then the workgroup barrier.
+__device__ __forceinline__ void lds_loads_done_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); other counters unconstrained
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: 4 wavefronts own one 128-row query tile of one head.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Kb, const uint16_t* __restrict__ Vb, void* __restrict__ Out,
-    float* __restrict__ LSE, int Hq, int Hkv, int n, int w, int G, int L, float scale_log2, int T) {
-  using LD = Lds<D>;
-  constexpr int KK = D / 32;  // k-steps of the QK^T contraction
-  constexpr int MB = D / 16;  // 16-dim blocks of O^T
-  __shared__ __align__(16) uint16_t lds[2 * LD::kBuf];
+    float* __restrict__ LSE, int Hq, int Hkv, int n, int w, int G, int L, float c2, int T) {
+  using SM = Smem<D>;
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
 
-  // ---- which (batch, head, query tile) this workgroup owns
   const int j = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = Hq / Hkv;
   const int h_in = j % grp;
   int rest = j / grp;
-  const int t = T - 1 - rest % T;  // heaviest tiles first
+  const int t = T - 1 - rest % T;
   rest /= T;
   const int kvh = rest % Hkv;
   const int b = rest / Hkv;
   const int h = kvh * grp + h_in;
 
-  const TileRange tr = tile_range(t, BM, BN, n, w, G, L);
-  const int n_win = tr.kt_hi - tr.kt_lo + 1;
-  const int n_tiles = tr.n_lm_tiles + n_win;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int r32 = lane & 31;
+  const int g2 = lane >> 5;
 
-  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)n * D;
-  const size_t lm_off = ((size_t)b * Hkv + kvh) * (size_t)(G > 0 ? G : 1) * D;
-  const size_t q_off = ((size_t)b * Hq + h) * (size_t)n * D;
-  const uint16_t* Kw = K + kv_off;
-  const uint16_t* Vw = V + kv_off;
-  const uint16_t* Kl = G > 0 ? Kb + lm_off : Kw;
-  const uint16_t* Vl = G > 0 ? Vb + lm_off : Vw;
+  zero_smem<D>(smem, tid, kThreads);
 
-  // ---- this wave's rows and its own sub-range of the tile list
-  const int wr0 = tr.r0 + wave * 32;
+  Walk<D> wk;
+  wk.init(K, V, Kb, Vb, b, Hkv, kvh, t, n, w, G, L);
+  const int n_tiles = wk.n_tiles;
+
+  const int wr0 = wk.tr.r0 + wave * 32;
   const int wr1 = min(wr0 + 31, n - 1);
-  const bool wave_live = wr0 <= n - 1;
-  int row[2];
-  int lmc[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    row[nb] = wr0 + nb * 16 + c16;
-    lmc[nb] = lm_count(row[nb], w, G, L);
-  }
+  const int row = wr0 + r32;
+  const int lmc = lm_count(row, w, G, L);
   const int wlm_lo = lm_count(wr0, w, G, L);
-  const int wlm_hi = wave_live ? lm_count(wr1, w, G, L) : 0;
+  const int wlm_hi = wr0 <= n - 1 ? lm_count(wr1, w, G, L) : 0;
+  const bool live = wr0 <= n - 1;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), held for the whole tile walk
-  bf16x8 qf[2][KK];
+  const size_t q_off = ((size_t)b * Hq + h) * (size_t)n * D;
+  bf16x8 qf[D / 16];
+  load_q<D>(Q, q_off, row, n, g2, qf);
+
+  RowState<D> st;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row[nb] < n) v = *reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row[nb] * D + kk * 32 + g4 * 8);
-      qf[nb][kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
+  st.m = -1e30f;
+  st.l = 0.f;
+  st.ls = 0.f;
 
-  f32x4 o[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    o[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m[2] = {-1e30f, -1e30f};  // running max, base-2 scaled units
-  float l[2] = {0.f, 0.f};        // this lane's share of the running sum
+  Stager<D> sg;
+  sg.init(tid);
+  Frag<D> fr;
+  fr.init(lane);
+  __syncthreads();  // zeroed buffers in place before any load lands
 
-  TileLoader<D> ld;
-  auto issue = [&](int it) {
-    if (it < tr.n_lm_tiles) {
-      ld.load(Kl, Vl, it * BN, G, tid);
-    } else {
-      ld.load(Kw, Vw, (tr.kt_lo + it - tr.n_lm_tiles) * BN, n, tid);
-    }
-  };
-
-  issue(0);
-  ld.store(lds, tid);
-  __syncthreads();
+  sg.issue_k(wk.ksrc(0), smem + SM::kbuf(0), wk.key0(0));
+  sg.issue_v(wk.vsrc(0), smem + SM::vbuf(0), wk.key0(0));
+  lds_loads_done_barrier();
 
   for (int it = 0; it < n_tiles; ++it) {
-    const bool more = it + 1 < n_tiles;
-    if (more) issue(it + 1);
-
-    const uint16_t* kt = lds + (it & 1) * LD::kBuf;
-    const uint16_t* vt = kt + LD::kTile;
-    const bool is_lm = it < tr.n_lm_tiles;
-    const int key0 = is_lm ? it * BN : (tr.kt_lo + it - tr.n_lm_tiles) * BN;
-
-    // Does this wave see anything in the tile, and without a mask?
-    bool any, interior;
-    if (is_lm) {
-      any = wave_live && key0 < wlm_hi;
-      interior = (key0 + BN) <= wlm_lo;
-    } else {
-      any = wave_live && key0 <= wr1 && key0 + BN - 1 >= wr0 - w + 1;
-      interior = key0 + BN - 1 <= wr0 && key0 >= wr1 - w + 1;
+    sg.issue_k(wk.ksrc(it + 1), smem + SM::kbuf((it + 1) & 1), wk.key0(it + 1));
+    sg.issue_v(wk.vsrc(it + 1), smem + SM::vbuf((it + 1) & 1), wk.key0(it + 1));
+    const TileVis v = tile_vis(wk.is_lm(it), wk.key0(it), wr0, wr1, wlm_lo, wlm_hi, w);
+    if (live && v.any) {
+      f32x16 s[2];
+      bf16x8 pf[4];
+      mma_phase<D, false, true>(nullptr, smem + SM::kbuf(it & 1), fr, qf, pf, st.o, s);
+      if (!v.interior) mask_tile(s, wk.is_lm(it), wk.key0(it), row, lmc, w, g2);
+      softmax_tile<D>(s, c2, st, pf);
+      mma_phase<D, true, false>(smem + SM::vbuf(it & 1), nullptr, fr, qf, pf, st.o, s);
     }
-
-    if (any) {
-      // ---- S^T = K Q^T : acc[kb][nb] holds keys kb*16 + g4*4 + (0..3) of row nb*16 + c16
-      f32x4 acc[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        acc[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(kt + (kb * 16 + c16) * LD::KS + kk * 32 + g4 * 8);
-          acc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], acc[kb][0], 0, 0, 0);
-          acc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], acc[kb][1], 0, 0, 0);
-        }
-      }
-
-      // ---- scale into base-2 units, mask edge tiles
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float s = acc[kb][nb][i] * scale_log2;
-            if (!interior) {
-              const int key = key0 + kb * 16 + g4 * 4 + i;
-              const bool vis = is_lm ? (key < lmc[nb]) : (key <= row[nb] && key > row[nb] - w);
-              s = vis ? s : -INFINITY;
-            }
-            acc[kb][nb][i] = s;
-          }
-        }
-      }
-
-      // ---- online softmax
-      float alpha[2];
-      bool rescale = false;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          mx = fmaxf(mx, fmaxf(fmaxf(acc[kb][nb][0], acc[kb][nb][1]), fmaxf(acc[kb][nb][2], acc[kb][nb][3])));
-        }
-        mx = wave_max16(mx);
-        const float m_new = fmaxf(m[nb], mx);
-        alpha[nb] = exp2f(m[nb] - m_new);
-        rescale |= m_new > m[nb];
-        m[nb] = m_new;
-      }
-      if (__any(rescale)) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          l[nb] *= alpha[nb];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) o[mb][nb] *= alpha[nb];
-        }
-      }
-
-      // P = exp2(s - m), packed to bf16 as the B operand of O^T += V^T P^T.
-      bf16x8 pf[2][2];  // [kb2][nb]
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float rs = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = exp2f(acc[2 * kb2][nb][i] - m[nb]);
-            p[4 + i] = exp2f(acc[2 * kb2 + 1][nb][i] - m[nb]);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) rs += p[i];
-          u32x4 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-          pf[kb2][nb] = __builtin_bit_cast(bf16x8, pk);
-        }
-        l[nb] += rs;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const uint16_t* vrow = vt + (mb * 16 + c16) * LD::VS + kb2 * 32 + g4 * 4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-          const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-          o[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kb2][0], o[mb][0], 0, 0, 0);
-          o[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kb2][1], o[mb][1], 0, 0, 0);
-        }
-      }
-    }
-
-    if (more) ld.store(lds + ((it + 1) & 1) * LD::kBuf, tid);
-    __syncthreads();
+    lds_loads_done_barrier();
   }
-
-  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float lt = wave_sum16(l[nb]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (row[nb] < n) {
-      const size_t base = q_off + (size_t)row[nb] * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int dcol = mb * 16 + g4 * 4;
-        const f32x4 v = o[mb][nb] * inv;
-        if constexpr (OUT_BF16) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + base + dcol) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + base + dcol) = v;
-        }
-      }
-      if (LSE != nullptr && g4 == 0) {
-        LSE[((size_t)b * Hq + h) * n + row[nb]] = (m[nb] + log2f(lt)) * kLn2;
-      }
-    }
-  }
+  store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
 }
 
 template <int D, bool OUT_BF16>
@@ -365,12 +484,14 @@ hipError_t launch_t(const msa_attn_desc& d, const void* Q, const void* K, const 
   const int T = (n + BM - 1) / BM;
   const int G = d.num_landmarks;
   const int L = G > 0 ? n / G : 1;
+  const auto q = static_cast<const uint16_t*>(Q);
+  const auto k = static_cast<const uint16_t*>(K);
+  const auto v = static_cast<const uint16_t*>(V);
+  const auto kb = static_cast<const uint16_t*>(Kb);
+  const auto vb = static_cast<const uint16_t*>(Vb);
   const long long wgs = (long long)d.batch * d.heads_q * T;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_BF16>), dim3((unsigned)wgs), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(Kb),
-                     static_cast<const uint16_t*>(Vb), O, LSE, d.heads_q, d.heads_kv, n, d.window, G, L,
-                     d.scale * kLog2e, T);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_BF16>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, q, k,
+                     v, kb, vb, O, LSE, d.heads_q, d.heads_kv, n, d.window, G, L, d.scale * kLog2e, T);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ def base_desc(**kw):
     (dict(window=0), 1), (dict(window=-3), 1), (dict(num_landmarks=-1), 1), (dict(num_landmarks=3), 1),
     (dict(heads_q=3), 1), (dict(heads_kv=0), 1), (dict(head_dim=96), 2), (dict(head_dim=256), 2),
     (dict(in_dtype=7), 1), (dict(out_dtype=5), 1), (dict(batch=-1), 1), (dict(seq_len=-5), 1),
-    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1), (dict(scale=-0.5), 1),
     (dict(in_dtype=msa.MSA_DTYPE_F32, out_dtype=msa.MSA_DTYPE_BF16), 2),
 ])
 def test_attn_validation(kw, status):
