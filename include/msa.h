@@ -69,7 +69,9 @@ typedef enum { MSA_DTYPE_F32 = 0, MSA_DTYPE_BF16 = 1 } msa_dtype;
 /* Prefill problem.  head_dim in {64, 128}.  window >= 1 (a window >= n is
  * plain causal attention).  num_landmarks G >= 0; G > 0 requires n % G == 0.
  * in_dtype is the dtype of Q, K, V, Kbar, Vbar; out_dtype that of O
- * (bf16 inputs may write float32 O; float32 inputs write float32 O). */
+ * (bf16 inputs may write float32 O; float32 inputs write float32 O).
+ * With bf16 inputs one head's K or V, seq_len*head_dim*2 bytes, must be
+ * < 2 GiB (MSA_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int32_t batch;
   int32_t heads_q;
@@ -130,14 +132,25 @@ msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes)
  * The ordered visible list of row ctx-1 (visible landmarks in block order,
  * then the window keys ascending; E entries) is cut into num_splits chunks
  * of s = ceil(E / num_splits) entries; chunk c covers [c*s, min(E,(c+1)*s)).
- * Pass 1 writes each chunk's normalised output and log-sum-exp into the
- * workspace: o_c float32 [S][B][Hq][d] at offset 0, then lse_c float32
- * [S][B][Hq] (an empty chunk has lse_c = -inf, o_c = 0).  Pass 2 merges:
+ * Each chunk's normalised output o_c and log-sum-exp lse_c (an empty chunk
+ * has lse_c = -inf, o_c = 0) are merged:
  * LSE = ln sum_c exp(lse_c), O = sum_c exp(lse_c - LSE) o_c.
+ * Two schedules compute this, with the same results up to float32 rounding
+ * of the merge:
+ *  - split: one wavefront per chunk writes (o_c, lse_c) to the workspace --
+ *    o_c float32 [S][B][Hq][d] at offset 0, then lse_c float32 [S][B][Hq] --
+ *    and a second kernel merges them;
+ *  - fused: one workgroup per (sequence, KV head) streams all its chunks,
+ *    merging the partials on chip; the workspace is not written.
+ * The fused schedule is used when batch*heads_kv >= 2 x (compute units) and
+ * num_splits >= 4; the environment variable MSA_DECODE_SCHEDULE=split|fused,
+ * read at each call, forces one of them.
  * The workspace is caller-owned scratch of at least
- * msa_decode_workspace_size() bytes; its contents after the call are the
- * partials described above.  Kbar/Vbar: landmarks of the caches (NULL if
- * G == 0).  LSE may be NULL.  in_dtype must be bf16 or f32. */
+ * msa_decode_workspace_size() bytes (required by both schedules).
+ * Kbar/Vbar: landmarks of the caches (NULL if G == 0).  LSE may be NULL.
+ * in_dtype must be bf16 (MSA_ERR_UNSUPPORTED otherwise); out_dtype bf16 or
+ * f32.  One head's cache, ctx_len*head_dim*2 bytes, must be < 2 GiB
+ * (MSA_ERR_UNSUPPORTED otherwise). */
 msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void* Kcache,
                           const void* Vcache, const void* Kbar, const void* Vbar, void* workspace,
                           size_t workspace_bytes, void* O, float* LSE, void* stream);

@@ -73,6 +73,15 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    # A kernel whose host-side launch stub was not emitted leaves an
+    # undefined stub symbol that only fails when the library is loaded with
+    # eager binding; refuse such a link here.
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    stubs = [ln.split()[-1] for ln in und.splitlines() if "__device_stub" in ln]
+    if stubs:
+        os.remove(tmp)
+        raise RuntimeError("link left kernel launch stubs undefined: " + ", ".join(stubs))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -79,6 +79,8 @@ msa_status check_attn(const msa_attn_desc* d) {
     return fail(MSA_ERR_UNSUPPORTED, "float32 inputs write float32 output only");
   const long long wgs = (long long)d->batch * d->heads_q * ((d->seq_len + 63) / 64);
   if (wgs > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (d->in_dtype == MSA_DTYPE_BF16 && (long long)d->seq_len * d->head_dim * 2 >= (1LL << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "seq_len=%d: one head's K or V must be < 2 GiB", d->seq_len);
   return MSA_OK;
 }
 
@@ -106,6 +108,8 @@ msa_status check_decode(const msa_decode_desc* d) {
     return fail(MSA_ERR_INVALID_ARG, "out_dtype=%d is not a msa_dtype", d->out_dtype);
   const long long wgs = (long long)d->batch * d->heads_kv * d->num_splits;
   if (wgs > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if ((long long)d->ctx_len * d->head_dim * 2 >= (1LL << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "ctx_len=%d: one head's cache must be < 2 GiB", d->ctx_len);
   return MSA_OK;
 }
 

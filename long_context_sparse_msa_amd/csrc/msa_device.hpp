@@ -30,6 +30,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// ds_read_b64_tr_b16 written as inline assembly.  For the builtin form the
+// compiler assumes the read may alias any direct-to-LDS buffer load still in
+// flight and puts a vmcnt(0) wait in front of it, which would stall every
+// tile on the prefetch of the next one.  The caller orders the read after
+// the loads of its own tile (wait + barrier) and waits for the result with
+// lds_wait() before using it.  `addr` is the LDS byte address.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
+// Wait until at most n LDS operations are outstanding (n a constant after
+// unrolling, 0..15).  LDS operations complete in issue order, so with n =
+// the number of LDS reads issued after the ones that produced x (and y),
+// their results are ready afterwards.  The values are tied to the wait:
+// every use of them, including any copy, comes after it.  Build operands
+// from the tied values only after this call.  x and y must be distinct
+// objects (the same object twice makes the compiler copy it before the wait).
+#define MSA_LGKM_SWITCH(n, ...)                                                          \
+  switch (n) {                                                                         \
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : __VA_ARGS__); break;                 \
+    case 1: asm volatile("s_waitcnt lgkmcnt(1)" : __VA_ARGS__); break;                 \
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" : __VA_ARGS__); break;                 \
+    case 3: asm volatile("s_waitcnt lgkmcnt(3)" : __VA_ARGS__); break;                 \
+    case 4: asm volatile("s_waitcnt lgkmcnt(4)" : __VA_ARGS__); break;                 \
+    case 5: asm volatile("s_waitcnt lgkmcnt(5)" : __VA_ARGS__); break;                 \
+    case 6: asm volatile("s_waitcnt lgkmcnt(6)" : __VA_ARGS__); break;                 \
+    case 7: asm volatile("s_waitcnt lgkmcnt(7)" : __VA_ARGS__); break;                 \
+    case 8: asm volatile("s_waitcnt lgkmcnt(8)" : __VA_ARGS__); break;                 \
+    case 9: asm volatile("s_waitcnt lgkmcnt(9)" : __VA_ARGS__); break;                 \
+    case 10: asm volatile("s_waitcnt lgkmcnt(10)" : __VA_ARGS__); break;               \
+    case 11: asm volatile("s_waitcnt lgkmcnt(11)" : __VA_ARGS__); break;               \
+    case 12: asm volatile("s_waitcnt lgkmcnt(12)" : __VA_ARGS__); break;               \
+    case 13: asm volatile("s_waitcnt lgkmcnt(13)" : __VA_ARGS__); break;               \
+    case 14: asm volatile("s_waitcnt lgkmcnt(14)" : __VA_ARGS__); break;               \
+    default: asm volatile("s_waitcnt lgkmcnt(15)" : __VA_ARGS__); break;               \
+  }
+
+template <typename T>
+__device__ __forceinline__ void lds_wait(int n, T& x) {
+  MSA_LGKM_SWITCH(n, "+v"(x))
+}
+template <typename T, typename U>
+__device__ __forceinline__ void lds_wait(int n, T& x, U& y) {
+  MSA_LGKM_SWITCH(n, "+v"(x), "+v"(y))
+}
+#undef MSA_LGKM_SWITCH
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // MI355X dispatches workgroup i to XCD (i mod 8).  Renumber so that the
 // workgroups an XCD runs are consecutive in the logical order, which keeps
 // the data they share inside that XCD's L2.  Bijective for any count.

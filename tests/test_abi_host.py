@@ -65,6 +65,7 @@ def base_desc(**kw):
     (dict(in_dtype=7), 1), (dict(out_dtype=5), 1), (dict(batch=-1), 1), (dict(seq_len=-5), 1),
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1), (dict(scale=-0.5), 1),
     (dict(in_dtype=msa.MSA_DTYPE_F32, out_dtype=msa.MSA_DTYPE_BF16), 2),
+    (dict(seq_len=1 << 23), 2), (dict(seq_len=1 << 24, head_dim=64), 2),
 ])
 def test_attn_validation(kw, status):
     assert call_attn(base_desc(**kw)) == status
@@ -100,7 +101,7 @@ def dec_desc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(num_splits=0), 1), (dict(window=0), 1), (dict(num_landmarks=7), 1), (dict(ctx_len=0), 1),
     (dict(heads_q=6, heads_kv=4), 1), (dict(heads_q=64, heads_kv=2), 2), (dict(head_dim=32), 2),
-    (dict(in_dtype=msa.MSA_DTYPE_F32), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32), 2), (dict(ctx_len=1 << 23), 2),
 ])
 def test_decode_validation(kw, status):
     d = dec_desc(**kw)

@@ -226,9 +226,11 @@ DEC = [
 ]
 
 
+@pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("B,Hq,Hkv,ctx,d,w,G,S", DEC)
-def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S):
-    print(f"[case] decode B={B} Hq={Hq} Hkv={Hkv} ctx={ctx} d={d} w={w} G={G} S={S}", flush=True)
+def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S, schedule, monkeypatch):
+    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+    print(f"[case] decode {schedule} B={B} Hq={Hq} Hkv={Hkv} ctx={ctx} d={d} w={w} G={G} S={S}", flush=True)
     q = rand((B, Hq, d), 9, torch.bfloat16)
     Kc = rand((B, Hkv, ctx, d), 10, torch.bfloat16)
     Vc = rand((B, Hkv, ctx, d), 11, torch.bfloat16)
@@ -245,6 +247,8 @@ def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S):
     o_ref, l_ref = orc.decode(q64, k64, v64, w, G, scale)
     assert_close(host64(O32), host64(L32), o_ref, l_ref, TOL_BF16, "decode merged")
     assert torch.equal(O16, bf16_rne(O32))
+    if schedule != "split":
+        return  # the fused schedule keeps the partials on chip
     # Per-chunk partials.  A chunk may hold a single landmark, whose score the
     # bf16 storage of the pooled landmark moves by up to ~1e-3 at short
     # blocks; chunks are therefore graded against the oracle fed with its
@@ -263,8 +267,10 @@ def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S):
         assert_close(po[~empty], pl[~empty], ro[~empty], rl[~empty], TOL_BF16, "decode chunks")
 
 
-def test_decode_equals_prefill_last_row():
-    print("[case] decode vs prefill row", flush=True)
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+def test_decode_equals_prefill_last_row(schedule, monkeypatch):
+    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+    print(f"[case] decode {schedule} vs prefill row", flush=True)
     B, Hq, Hkv, n, d, w, G = 2, 8, 2, 2048, 128, 200, 16
     Q = rand((B, Hq, n, d), 12, torch.bfloat16)
     K = rand((B, Hkv, n, d), 13, torch.bfloat16)
@@ -279,14 +285,21 @@ def test_decode_equals_prefill_last_row():
         assert (Ld - L[:, :, -1]).abs().max().item() < 1e-4
 
 
-def test_decode_workload_512k():
+def test_decode_workload_512k(monkeypatch):
     cfg = wl.DECODE_512K
     print(f"[case] {cfg.name}", flush=True)
     q, Kc, Vc = wl.device_decode_inputs(cfg, dev())
     Kb, Vb = msa.msa_pool_landmarks(Kc, Vc, cfg.num_landmarks)
-    O32, L32 = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, cfg.window, cfg.num_landmarks, cfg.num_splits,
-                                  cfg.scale, out_dtype=torch.float32)
-    O16, _ = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, cfg.window, cfg.num_landmarks, cfg.num_splits, cfg.scale)
+    desc = msa.decode_desc(cfg.batch, cfg.heads_q, cfg.heads_kv, cfg.ctx_len, cfg.head_dim, cfg.window,
+                           cfg.num_landmarks, cfg.num_splits, cfg.scale, msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_F32)
+    ws = torch.empty(msa.msa_decode_workspace_size(desc) // 4, dtype=torch.float32, device=dev())
+    args = (q, Kc, Vc, Kb, Vb, cfg.window, cfg.num_landmarks, cfg.num_splits, cfg.scale)
+    O32, L32 = msa.msa_decode_fwd(*args, out_dtype=torch.float32)   # the schedule bench times
+    O16, _ = msa.msa_decode_fwd(*args)
+    monkeypatch.setenv("MSA_DECODE_SCHEDULE", "split")
+    Os, Ls = msa.msa_decode_fwd(*args, out_dtype=torch.float32, workspace=ws)
+    po, pl = msa.decode_partials(ws, cfg.num_splits, cfg.batch, cfg.heads_q, cfg.head_dim)
+    po, pl = host64(po[:, 0]), host64(pl[:, 0])
     torch.cuda.synchronize()
     assert torch.equal(O16, bf16_rne(O32))
     for b in (0, cfg.batch - 1):
@@ -294,6 +307,14 @@ def test_decode_workload_512k():
         o_ref, l_ref = orc.decode(host64(q[b:b + 1]), k64, v64, cfg.window, cfg.num_landmarks, cfg.scale)
         assert_close(host64(O32[b:b + 1]), host64(L32[b:b + 1]), o_ref, l_ref, TOL_BF16,
                      f"{cfg.name} seq {b} (64 heads)")
+        assert_close(host64(Os[b:b + 1]), host64(Ls[b:b + 1]), o_ref, l_ref, TOL_BF16,
+                     f"{cfg.name} seq {b} (64 heads), split schedule")
+        if b == 0:
+            kb_r = host64(torch.from_numpy(orc.pool(k64, cfg.num_landmarks)).to(torch.bfloat16))
+            vb_r = host64(torch.from_numpy(orc.pool(v64, cfg.num_landmarks)).to(torch.bfloat16))
+            ro, rl = orc.decode_partials(host64(q[:1]), k64, v64, cfg.window, cfg.num_landmarks, cfg.num_splits,
+                                         cfg.scale, Kbar=kb_r, Vbar=vb_r)
+            assert_close(po, pl, ro[:, 0], rl[:, 0], TOL_BF16, f"{cfg.name} seq 0 chunk partials")
         del k64, v64
     del q, Kc, Vc, Kb, Vb
     torch.cuda.empty_cache()
