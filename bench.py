@@ -81,21 +81,22 @@ def summarize_pmc(fetch_csv, write_csv):
 
     fs, ws = calib(fetch), calib(write)
     out = {}
-    for key, needle, srcs in (("attn_fwd_gqa_128k", "attn_fwd_bf16_kernel",
-                               ["attn_bf16.hip", "msa_plan.hpp", "msa_device.hpp"]),
-                              ("decode_512k", "decode_split_kernel", ["decode.hip", "msa_plan.hpp", "msa_device.hpp"])):
-        fv = [v for (name, v) in fetch.values() if needle in name]
-        wv = [v for (name, v) in write.values() if needle in name]
-        if key.startswith("decode"):
-            fv += [v for (name, v) in fetch.values() if "decode_merge_kernel" in name][: len(fv)]
-            wv += [v for (name, v) in write.values() if "decode_merge_kernel" in name][: len(wv)]
-            nl = max(1, len([1 for (name, _) in fetch.values() if needle in name]))
-        else:
-            nl = max(1, len(fv))
-        fb = sum(fv) * 1024.0 * fs / nl
-        wb = sum(wv) * 1024.0 * ws / max(1, len([1 for (name, _) in write.values() if needle in name]))
+    # (profile key, kernels whose traffic counts, kernels that mark one call, sources)
+    for key, parts, primary, srcs in (
+            ("attn_fwd_gqa_128k", ("attn_fwd_bf16_kernel",), ("attn_fwd_bf16_kernel",),
+             ["attn_bf16.hip", "msa_plan.hpp", "msa_device.hpp"]),
+            ("decode_512k", ("decode_fused_kernel", "decode_split_kernel", "decode_merge_kernel"),
+             ("decode_fused_kernel", "decode_split_kernel"), ["decode.hip", "msa_plan.hpp", "msa_device.hpp"])):
+        def total(rows):
+            return sum(v for (name, v) in rows.values() if any(p in name for p in parts))
+
+        def calls(rows):
+            return max(1, sum(1 for (name, _) in rows.values() if any(p in name for p in primary)))
+
+        fb = total(fetch) * 1024.0 * fs / calls(fetch)
+        wb = total(write) * 1024.0 * ws / calls(write)
         rec = {"source_hash": kernel_hash(*srcs), "fetch_bytes": fb, "write_bytes": wb,
-               "bytes_per_launch": fb + wb, "fetch_scale": fs, "write_scale": ws, "launches": nl}
+               "bytes_per_launch": fb + wb, "fetch_scale": fs, "write_scale": ws, "launches": calls(fetch)}
         with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         out[key] = rec
