@@ -399,6 +399,33 @@ __device__ __forceinline__ void lds_loads_done_barrier() {
   __syncthreads();
 }
 
+// Per-wavefront constants of the walk.
+struct TileCtx {
+  int wr0, wr1, wlm_lo, wlm_hi, w, row, lmc, g2;
+  bool live;
+  float c2;
+};
+
+// One tile of the walk: issue the next tile's loads into the other buffer,
+// then scores, mask, softmax and PV from buffer BUF (= it & 1).
+template <int D, int BUF>
+__device__ __forceinline__ void tile_step(int it, unsigned char* smem, const Stager<D>& sg, const Walk<D>& wk,
+                                          const Frag<D>& fr, const bf16x8* qf, RowState<D>& st, const TileCtx& tc) {
+  using SM = Smem<D>;
+  sg.issue_k(wk.ksrc(it + 1), smem + SM::kbuf(BUF ^ 1), wk.key0(it + 1));
+  sg.issue_v(wk.vsrc(it + 1), smem + SM::vbuf(BUF ^ 1), wk.key0(it + 1));
+  const TileVis v = tile_vis(wk.is_lm(it), wk.key0(it), tc.wr0, tc.wr1, tc.wlm_lo, tc.wlm_hi, tc.w);
+  if (tc.live && v.any) {
+    f32x16 s[2];
+    bf16x8 pf[4];
+    mma_phase<D, false, true>(nullptr, smem + SM::kbuf(BUF), fr, qf, pf, st.o, s);
+    if (!v.interior) mask_tile(s, wk.is_lm(it), wk.key0(it), tc.row, tc.lmc, tc.w, tc.g2);
+    softmax_tile<D>(s, tc.c2, st, pf);
+    mma_phase<D, true, false>(smem + SM::vbuf(BUF), nullptr, fr, qf, pf, st.o, s);
+  }
+  lds_loads_done_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // The kernel: 4 wavefronts own one 128-row query tile of one head.
 template <int D, bool OUT_BF16>
@@ -460,20 +487,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   sg.issue_v(wk.vsrc(0), smem + SM::vbuf(0), wk.key0(0));
   lds_loads_done_barrier();
 
-  for (int it = 0; it < n_tiles; ++it) {
-    sg.issue_k(wk.ksrc(it + 1), smem + SM::kbuf((it + 1) & 1), wk.key0(it + 1));
-    sg.issue_v(wk.vsrc(it + 1), smem + SM::vbuf((it + 1) & 1), wk.key0(it + 1));
-    const TileVis v = tile_vis(wk.is_lm(it), wk.key0(it), wr0, wr1, wlm_lo, wlm_hi, w);
-    if (live && v.any) {
-      f32x16 s[2];
-      bf16x8 pf[4];
-      mma_phase<D, false, true>(nullptr, smem + SM::kbuf(it & 1), fr, qf, pf, st.o, s);
-      if (!v.interior) mask_tile(s, wk.is_lm(it), wk.key0(it), row, lmc, w, g2);
-      softmax_tile<D>(s, c2, st, pf);
-      mma_phase<D, true, false>(smem + SM::vbuf(it & 1), nullptr, fr, qf, pf, st.o, s);
-    }
-    lds_loads_done_barrier();
+  // Two tiles per trip, so each one's LDS buffer is a compile-time offset
+  // that the operand reads take as an immediate.
+  const TileCtx tc{wr0, wr1, wlm_lo, wlm_hi, w, row, lmc, g2, live, c2};
+  int it = 0;
+  for (; it + 1 < n_tiles; it += 2) {
+    tile_step<D, 0>(it, smem, sg, wk, fr, qf, st, tc);
+    tile_step<D, 1>(it + 1, smem, sg, wk, fr, qf, st, tc);
   }
+  if (it < n_tiles) tile_step<D, 0>(it, smem, sg, wk, fr, qf, st, tc);
   store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
 }
 
