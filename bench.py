@@ -158,6 +158,67 @@ def cpu_baseline(cfg, Q, K, V, rows_per_head, heads):
     }
 
 
+def prefill_1m(torch, msa, wl, dev, stream, reps=3):
+    """Secondary line: pooling + prefill of the 1M-token GQA workload."""
+    cfg = wl.GQA_1M
+    Q, K, V = wl.device_prefill_inputs(cfg, dev)
+    G = cfg.num_landmarks
+    Kb = torch.empty((cfg.batch, cfg.heads_kv, G, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    Vb = torch.empty_like(Kb)
+    O = torch.empty(Q.shape, dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    run = lambda: (msa.msa_pool_landmarks(K, V, G, Kb, Vb),
+                   msa.msa_attn_fwd(Q, K, V, Kb, Vb, cfg.window, G, cfg.scale, O=O, LSE=LSE))
+    run()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        run()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / reps
+    win, lm = visible_pairs(cfg.seq_len, cfg.window, G)
+    flops = 4.0 * cfg.head_dim * (win + lm) * cfg.heads_q * cfg.batch
+    del Q, K, V, O, LSE, Kb, Vb
+    torch.cuda.empty_cache()
+    return {"workload": "gqa_1m (n=1048576, 64/8 heads, d=128, w=4096, G=512), pooling + prefill",
+            "ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
+
+
+def measured_peaks(torch, dev, reps=10):
+    """Achievable references on this GPU through vendor libraries: a large
+    bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e[1].record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * 8192 ** 3 / (e[0].elapsed_time(e[1]) / reps * 1e-3) / 1e12
+    del a, b, c
+    x = torch.empty(1 << 30, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(reps):
+        y.copy_(x)
+    e[1].record()
+    torch.cuda.synchronize()
+    copy = 2.0 * x.numel() * 2 / (e[0].elapsed_time(e[1]) / reps * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": round(gemm, 1), "bf16_gemm_shape": "8192^3 (torch.matmul)",
+            "hbm_copy_gbs": round(copy, 1), "hbm_copy": "2 GiB device copy, read + write bytes"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=49152, help="oracle rows per head for the CPU baseline")
+    ap.add_argument("--no-1m", action="store_true", help="skip the secondary 1M-token prefill measurement")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured achievable-peak reference runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device-to-device copy before timing (reference dispatch for HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -222,29 +285,45 @@ def main():
     cache_pool_ms = e0.elapsed_time(e1)
     cache_bytes = 2 * Kc.numel() * 2 + 2 * Kbc.numel() * 2
 
+    # 512 MiB read (not written: evicting dirty lines would slow the decode
+    # that follows) before each decode call, so the 256 MB last-level cache
+    # holds nothing of the cache the decode streams
+    flush = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
     def step(ev):
         ev[0].record(stream)
         msa.msa_pool_landmarks(K, V, G, Kb, Vb)
         ev[1].record(stream)
         msa.msa_attn_fwd(Q, K, V, Kb, Vb, pre.window, G, pre.scale, O=O, LSE=LSE)
         ev[2].record(stream)
+        torch.sum(flush, dim=(0,), dtype=torch.float32, out=flush_sink)
+        ev[3].record(stream)
         msa.msa_decode_fwd(q, Kc, Vc, Kbc, Vbc, dec.window, dec.num_landmarks, dec.num_splits, dec.scale,
                            workspace=ws, O=Od, LSE=Ld)
-        ev[3].record(stream)
+        ev[4].record(stream)
 
     for _ in range(args.warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    pool_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    pool_t = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_t = [e[1].elapsed_time(e[2]) for e in evs]
+    dec_t = [e[3].elapsed_time(e[4]) for e in evs]
+    pool_ms = sum(pool_t) / args.steps
+    attn_ms = sum(attn_t) / args.steps
+    dec_ms = sum(dec_t) / args.steps
+
+    def stats(ts):
+        ts = sorted(ts)
+        return {"mean": round(sum(ts) / len(ts), 4), "median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4)}
 
     # ---- algorithmic work
     win_pairs, lm_pairs = visible_pairs(n, pre.window, G)
@@ -309,13 +388,20 @@ def main():
             "cache_ms": round(cache_pool_ms, 4),
             "cache_GBps": round(cache_bytes / (cache_pool_ms * 1e-3) / 1e9, 1),
         },
-        "kernels_ms": {"pool": round(pool_ms, 4), "attn_fwd": round(attn_ms, 4), "decode": round(dec_ms, 4)},
+        "kernels_ms": {"pool": stats(pool_t), "attn_fwd": stats(attn_t), "decode": stats(dec_t)},
         "useful_pairs_per_head": {"window": win_pairs, "landmark": lm_pairs},
         "cpu_baseline": None,
     }
 
-    del q, Kc, Vc, ws
+    del q, Kc, Vc, ws, flush, flush_sink
     torch.cuda.empty_cache()
+    if not args.no_1m:
+        out["prefill_1m"] = prefill_1m(torch, msa, wl, dev, stream)
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, dev)
+        out["measured_peaks"] = peaks
+        out["roofline"]["frac_of_measured"] = round(attn_tflops / peaks["bf16_gemm_tflops"], 4)
+        out["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / peaks["hbm_copy_gbs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, Q, K, V, args.cpu_rows, list(range(8)))
     print(json.dumps(out), flush=True)
