@@ -35,6 +35,13 @@ Readings taken where the pages leave the step open:
   form of the softmax-statistics aggregation in the Ring Attention paragraph
   of the "Training at 1M+ Token Context" page.
 
+* Incremental decode (sequences of different lengths in one cache, one
+  token appended per step): the block length L is fixed by the cache's
+  capacity, a landmark is the mean of its block once all L rows are in the
+  cache, and the visibility rule is unchanged, so a visible landmark is
+  always a complete block.  With every length equal to the capacity this is
+  the decode above.  A sequence of length 0 has O = 0 and LSE = -inf.
+
 Every predicate below is evaluated by explicit comparisons; nothing uses a
 closed-form count of visible keys.
 """
@@ -378,3 +385,104 @@ def decode(q, Kc, Vc, w: int, G: int, scale: Optional[float] = None, Kbar=None, 
     Returns (O [B, Hq, d], LSE [B, Hq])."""
     o, lse = decode_partials(q, Kc, Vc, w, G, 1, scale, Kbar, Vbar)
     return o[0], lse[0]
+
+
+# ---------------------------------------------------------------------------
+# Step 7: incremental decode -- sequences of different lengths that grow one
+# token at a time ("Million Token Context Window Optimization: What Actually
+# Works", section "Flash MSA vs Flash Attention: The real difference":
+# generation continues after the long prompt; section "Benchmarking your
+# optimization": the KV cache is the per-token state).  Reading where the
+# pages are silent: the landmark block length L is fixed; landmark b is the
+# mean of rows bL .. bL+L-1 and exists once that block is complete; the
+# visibility rule is the one above, so a visible landmark is always a
+# complete block.  With every length equal to G*L this is decode() above.
+# ---------------------------------------------------------------------------
+
+def pool_prefix(X, n: int, L: int, G_cap: int):
+    """Landmarks of the first n rows of X [B, H, >=n, d] with block length L:
+    [B, H, G_cap, d], complete blocks b < n // L hold the block mean (fp64),
+    the others are zero (they are never visible)."""
+    X = np.asarray(X, dtype=np.float64)
+    B, H, _, d = X.shape
+    out = np.zeros((B, H, G_cap, d))
+    nb = min(n // L, G_cap)
+    if nb:
+        out[:, :, :nb] = X[:, :, :nb * L].reshape(B, H, nb, L, d).mean(axis=3)
+    return out
+
+
+def visible_list_fixed(i: int, w: int, L: int, G_cap: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Ordered visible entries of row i with fixed block length L: landmarks
+    b < G_cap with (b+1)*L - 1 <= i - w in block order, then the window keys
+    i-w < j <= i ascending.  Returns (kinds, idx) as visible_list()."""
+    lm = np.arange(G_cap)
+    lm = lm[landmark_visible(i, lm, L, w)] if G_cap else lm
+    keys = np.arange(max(0, i - w), i + 1)
+    keys = keys[window_visible(i, keys, w)]
+    kinds = np.concatenate([np.zeros(len(lm), np.int64), np.ones(len(keys), np.int64)])
+    return kinds, np.concatenate([lm, keys]).astype(np.int64)
+
+
+def decode_varlen_partials(q, Kc, Vc, ctx_lens, w: int, L: int, G_cap: int, S: int,
+                           scale: Optional[float] = None, Kbar=None, Vbar=None):
+    """Per-chunk decode results when sequence b holds ctx_lens[b] tokens of a
+    cache [B, Hkv, C, d] (query position ctx_lens[b]-1), landmark blocks of
+    fixed length L.  Landmarks are pooled from each sequence's own prefix
+    unless given ([B, Hkv, G_cap, d]).  Chunking per sequence as in
+    chunk_bounds().  Returns (o [S, B, Hq, d], lse [S, B, Hq])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = Kc.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((S, B, Hq, d))
+    lse = np.full((S, B, Hq), NEG_INF)
+    for b in range(B):
+        n = int(ctx_lens[b])
+        kinds, idx = visible_list_fixed(n - 1, w, L, G_cap)
+        bnd = chunk_bounds(len(idx), S)
+        kc_b = np.asarray(Kc[b:b + 1, :, :n], np.float64)
+        vc_b = np.asarray(Vc[b:b + 1, :, :n], np.float64)
+        kb_b = pool_prefix(kc_b, n, L, G_cap)[0] if Kbar is None else np.asarray(Kbar[b], np.float64)
+        vb_b = pool_prefix(vc_b, n, L, G_cap)[0] if Vbar is None else np.asarray(Vbar[b], np.float64)
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            s_all, v_all = _entries(q[b, h], kc_b[0, g], vc_b[0, g], kb_b[g], vb_b[g], kinds, idx, scale)
+            for c in range(S):
+                a, e = int(bnd[c]), int(bnd[c + 1])
+                if e <= a:
+                    continue
+                sc = s_all[a:e]
+                m = sc.max()
+                p = np.exp(sc - m)
+                l = p.sum()
+                o[c, b, h] = (p @ v_all[a:e]) / l
+                lse[c, b, h] = m + np.log(l)
+    return o, lse
+
+
+def decode_varlen(q, Kc, Vc, ctx_lens, w: int, L: int, G_cap: int, scale: Optional[float] = None,
+                  Kbar=None, Vbar=None):
+    """Unsplit incremental decode.  Returns (O [B, Hq, d], LSE [B, Hq])."""
+    o, lse = decode_varlen_partials(q, Kc, Vc, ctx_lens, w, L, G_cap, 1, scale, Kbar, Vbar)
+    return o[0], lse[0]
+
+
+def append_tokens(Kc, Vc, Kbar, Vbar, positions, k_new, v_new, L: int):
+    """Reference semantics of appending one token per sequence, in place on
+    float64 arrays: row positions[b] of every KV head takes k_new[b] and
+    v_new[b]; a sequence whose append completes block blk = (pos+1)/L - 1
+    gets that block's landmark recomputed as the mean of its L rows.
+    Positions outside [0, C) leave the sequence unchanged."""
+    B, Hkv, C, d = Kc.shape
+    for b in range(B):
+        pos = int(positions[b])
+        if pos < 0 or pos >= C:
+            continue
+        Kc[b, :, pos] = k_new[b]
+        Vc[b, :, pos] = v_new[b]
+        if (pos + 1) % L == 0 and (pos + 1) // L <= Kbar.shape[2]:
+            blk = (pos + 1) // L - 1
+            Kbar[b, :, blk] = Kc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
+            Vbar[b, :, blk] = Vc[b, :, blk * L:(blk + 1) * L].mean(axis=1)

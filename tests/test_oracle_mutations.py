@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import msa_oracle as orc
+from tests import test_oracle_incremental as inc
 from tests import test_oracle_pins as pins
 
 
@@ -56,6 +57,26 @@ def _merge_unweighted(o, lse):
     return O, orc.__dict__["_orig_merge"](o, lse)[1]
 
 
+def _varlen_query_past_end(i, w, L, G_cap):   # decodes row n instead of n-1
+    return orc.__dict__["_orig_vlf"](i + 1, w, L, G_cap)
+
+
+def _pool_prefix_sum(X, n, L, G_cap):          # sum instead of mean
+    return orc.__dict__["_orig_pool_prefix"](X, n, L, G_cap) * L
+
+
+def _append_at_block_start(Kc, Vc, Kbar, Vbar, positions, k_new, v_new, L):
+    # refreshes a landmark when its block's first row arrives, not its last
+    for b, pos in enumerate(positions):
+        pos = int(pos)
+        if 0 <= pos < Kc.shape[2]:
+            Kc[b, :, pos], Vc[b, :, pos] = k_new[b], v_new[b]
+            if pos % L == 0:
+                blk = pos // L
+                Kbar[b, :, blk] = Kc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
+                Vbar[b, :, blk] = Vc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
+
+
 MUTANTS = {
     "window_wide": ("window_visible", _window_wide),
     "window_no_self": ("window_visible", _window_no_self),
@@ -66,6 +87,9 @@ MUTANTS = {
     "softmax_drop_landmark_mass": ("_softmax_rows", _softmax_drop_landmark_mass),
     "lse_log2": ("_softmax_rows", _softmax_log2),
     "merge_unweighted": ("merge", _merge_unweighted),
+    "varlen_query_past_end": ("visible_list_fixed", _varlen_query_past_end),
+    "pool_prefix_sum": ("pool_prefix", _pool_prefix_sum),
+    "append_at_block_start": ("append_tokens", _append_at_block_start),
 }
 
 PIN_SET = [
@@ -80,6 +104,10 @@ PIN_SET = [
     lambda: pins.test_split_merge_any_partition(),
     lambda: pins.test_decode_equals_prefill_last_row(256, 64, 16),
     lambda: pins.test_window_one_no_landmarks_is_identity(),
+    lambda: inc.test_varlen_equals_prefill_row_of_padded_sequence(17, 3, 4),
+    lambda: inc.test_varlen_window_covers_everything_is_textbook_causal(9),
+    lambda: inc.test_append_builds_closed_form_landmarks(),
+    lambda: inc.test_append_then_decode_equals_decode_of_the_whole_prefix(),
 ]
 
 
@@ -88,7 +116,7 @@ def _failures():
     for pin in PIN_SET:
         try:
             pin()
-        except AssertionError:
+        except Exception:  # a wrong value or a crash: either way the pin caught it
             n += 1
     return n
 
@@ -103,5 +131,7 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(orc.__dict__, "_orig_pool", orc.pool)
     monkeypatch.setitem(orc.__dict__, "_orig_softmax", orc._softmax_rows)
     monkeypatch.setitem(orc.__dict__, "_orig_merge", orc.merge)
+    monkeypatch.setitem(orc.__dict__, "_orig_vlf", orc.visible_list_fixed)
+    monkeypatch.setitem(orc.__dict__, "_orig_pool_prefix", orc.pool_prefix)
     monkeypatch.setattr(orc, attr, fn)
     assert _failures() > 0, f"no pin caught the planted mistake {name}"
