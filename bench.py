@@ -187,6 +187,58 @@ def prefill_1m(torch, msa, wl, dev, stream, reps=3):
             "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
 
 
+def incremental_decode(torch, msa, wl, dec, dev, stream, q, Kc, Vc, Kbc, Vbc, ws, Od, Ld, flush, flush_sink,
+                       reps=5):
+    """Secondary line: one serving step on the decode caches holding
+    sequences of different lengths (seeded, uniform in [ctx/2, ctx]): append
+    one token per sequence (msa_append_kv), then decode every sequence at
+    its new length (msa_decode_fwd_varlen), the last-level cache flushed by
+    a read before each decode.  The appended row is the same at every
+    repetition, so the state does not drift.  Also times an append in which
+    every sequence completes a landmark block (its worst case)."""
+    lens = wl.decode_lengths(dec.batch, dec.ctx_len - 1)          # room for the appended token
+    pos_d = torch.from_numpy(lens).to(dev)
+    lens_d = pos_d + 1
+    B, Hkv, d = dec.batch, dec.heads_kv, dec.head_dim
+    k_new = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+    v_new = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+    G = dec.num_landmarks
+    L = dec.ctx_len // G
+    block_end = torch.from_numpy(((lens // L) * L + L - 1).astype("int32")).to(dev)  # completes a block
+
+    def once(ev):
+        torch.sum(flush, dim=(0,), dtype=torch.float32, out=flush_sink)
+        ev[0].record(stream)
+        msa.msa_append_kv(k_new, v_new, pos_d, Kc, Vc, Kbc, Vbc, G)
+        ev[1].record(stream)
+        msa.msa_decode_fwd_varlen(q, Kc, Vc, Kbc, Vbc, lens_d, dec.window, G, dec.num_splits, dec.scale,
+                                  workspace=ws, O=Od, LSE=Ld)
+        ev[2].record(stream)
+        msa.msa_append_kv(k_new, v_new, block_end, Kc, Vc, Kbc, Vbc, G)
+        ev[3].record(stream)
+
+    once([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for ev in evs:
+        once(ev)
+    torch.cuda.synchronize()
+    app = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+    dms = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
+    blk = sum(e[2].elapsed_time(e[3]) for e in evs) / reps
+    ddesc = msa.decode_desc(B, dec.heads_q, Hkv, dec.ctx_len, d, dec.window, G, dec.num_splits)
+    entries = sum(msa.msa_plan_decode_varlen(ddesc, int(n) + 1)[2] for n in lens)
+    nbytes = Hkv * entries * d * 2 * 2 + B * dec.heads_q * (d * 2 * 2 + 4)
+    gbs = nbytes / (dms * 1e-3) / 1e9
+    return {"workload": f"{B} sequences in a {dec.ctx_len}-token cache, lengths uniform in "
+                        f"[{dec.ctx_len // 2}, {dec.ctx_len}) (seeded), {dec.num_splits} chunks; "
+                        "append one token per sequence, then decode at the new lengths",
+            "decode_ms": round(dms, 4), "decode_GBps": round(gbs, 1),
+            "decode_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes,
+            "mean_length": round(float(lens.mean()) + 1, 1),
+            "append_ms": round(app, 4), "append_block_ms": round(blk, 4),
+            "append_block_bytes": int(B * Hkv * 2 * L * d * 2), "launches": reps}
+
+
 def measured_peaks(torch, dev, reps=10):
     """Achievable references on this GPU through vendor libraries: a large
     bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
@@ -228,6 +280,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=49152, help="oracle rows per head for the CPU baseline")
     ap.add_argument("--no-1m", action="store_true", help="skip the secondary 1M-token prefill measurement")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured achievable-peak reference runs")
+    ap.add_argument("--no-incremental", action="store_true",
+                    help="skip the secondary incremental-decode (append + varlen decode) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device-to-device copy before timing (reference dispatch for HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -393,6 +447,9 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_incremental:
+        out["incremental_decode"] = incremental_decode(torch, msa, wl, dec, dev, stream, q, Kc, Vc, Kbc, Vbc, ws,
+                                                       Od, Ld, flush, flush_sink)
     del q, Kc, Vc, ws, flush, flush_sink
     torch.cuda.empty_cache()
     if not args.no_1m:

@@ -53,7 +53,9 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+/* 1: pooling, prefill, static decode and plans.  2: adds incremental
+ * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen). */
+#define MSA_ABI_VERSION 2
 
 typedef enum {
   MSA_OK = 0,
@@ -155,6 +157,49 @@ msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void
                           const void* Vcache, const void* Kbar, const void* Vbar, void* workspace,
                           size_t workspace_bytes, void* O, float* LSE, void* stream);
 
+/* ---- Incremental decode: sequences of different lengths in one cache,
+ * grown one token per step.  The pages run generation after a long prompt
+ * with the KV cache as the per-token state ("Million Token Context Window
+ * Optimization: What Actually Works", sections "Flash MSA vs Flash
+ * Attention: The real difference" and "Benchmarking your optimization").
+ * Here the cache of every sequence has the same capacity C = desc->ctx_len
+ * rows ([B][Hkv][C][d], as above), landmark blocks have the fixed length
+ * L = C / G (G = desc->num_landmarks slots per sequence, [B][Hkv][G][d]),
+ * and a landmark is the mean of its block once the block's L rows are in
+ * the cache.  The visibility rule is the one at the top of this file, so a
+ * visible landmark is always a complete block. ---- */
+
+/* Decode of sequence b at its own length n_b = ctx_lens[b] (int32 device
+ * array [B], 4-byte aligned): its query, at position n_b-1, sees the window
+ * keys n_b-w .. n_b-1 and the landmarks b' with (b'+1)*L - 1 <= n_b-1-w.
+ * Its visible list is chunked, computed and merged exactly as in
+ * msa_decode_fwd (same schedules, same workspace size and layout, same
+ * MSA_DECODE_SCHEDULE override).  Only rows < n_b of the caches and
+ * landmark slots < (n_b - w)/L are read.  n_b is clamped to [0, C] on the
+ * device (the host cannot read it); n_b = 0 gives O = 0 and LSE = -inf.
+ * With every n_b = C this is msa_decode_fwd.  Other arguments and errors as
+ * for msa_decode_fwd. */
+msa_status msa_decode_fwd_varlen(const msa_decode_desc* desc, const int32_t* ctx_lens, const void* q,
+                                 const void* Kcache, const void* Vcache, const void* Kbar,
+                                 const void* Vbar, void* workspace, size_t workspace_bytes, void* O,
+                                 float* LSE, void* stream);
+
+/* Append one token per sequence: k_new, v_new [B][Hkv][d] (bf16) are stored
+ * at row p_b = positions[b] (int32 device array [B], 4-byte aligned) of
+ * Kcache and Vcache; when p_b + 1 is a multiple of L, landmark slot
+ * (p_b + 1)/L - 1 of Kbar and Vbar is set to the mean of that block's L
+ * rows, computed by the same code and in the same order as
+ * msa_pool_landmarks, so its bits equal pooling the finished cache.  A
+ * position outside [0, C) leaves sequence b untouched (use -1 for an idle
+ * slot).  Rows other than p_b and the other landmark slots are not written.
+ * Fields read: batch, heads_kv, ctx_len (= C), head_dim, num_landmarks,
+ * in_dtype (bf16 only, MSA_ERR_UNSUPPORTED otherwise).  Kbar/Vbar may be
+ * NULL when G == 0.  The caller appends position n_b before decoding with
+ * length n_b + 1 on the same stream. */
+msa_status msa_append_kv(const msa_decode_desc* desc, const int32_t* positions, const void* k_new,
+                         const void* v_new, void* Kcache, void* Vcache, void* Kbar, void* Vbar,
+                         void* stream);
+
 /* ---- Host-only introspection: the exact schedule the kernels use.  These
  * make no HIP call and need no GPU; all pointers are host memory. ---- */
 
@@ -176,6 +221,11 @@ msa_status msa_plan_tiles(const msa_attn_desc* desc, int32_t* out, int64_t capac
  * chunks), *lm_visible = visible landmarks of row ctx-1, *entries = E. */
 msa_status msa_plan_decode(const msa_decode_desc* desc, int32_t* chunk_bounds,
                            int32_t* lm_visible, int32_t* entries);
+
+/* Decode schedule of one sequence of ctx tokens (0 <= ctx <= desc->ctx_len)
+ * as msa_decode_fwd_varlen runs it: outputs as for msa_plan_decode. */
+msa_status msa_plan_decode_varlen(const msa_decode_desc* desc, int32_t ctx, int32_t* chunk_bounds,
+                                  int32_t* lm_visible, int32_t* entries);
 
 /* Static description of a status code. */
 const char* msa_status_string(msa_status s);

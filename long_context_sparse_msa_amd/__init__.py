@@ -15,10 +15,13 @@ from .binding import (  # noqa: F401
     decode_desc,
     decode_partials,
     lib,
+    msa_append_kv,
     msa_attn_fwd,
     msa_decode_fwd,
+    msa_decode_fwd_varlen,
     msa_decode_workspace_size,
     msa_plan_decode,
+    msa_plan_decode_varlen,
     msa_plan_rows,
     msa_plan_tiles,
     msa_pool_landmarks,
@@ -27,3 +30,5 @@ from .binding import (  # noqa: F401
 pool_landmarks = msa_pool_landmarks
 attn_fwd = msa_attn_fwd
 decode_fwd = msa_decode_fwd
+decode_fwd_varlen = msa_decode_fwd_varlen
+append_kv = msa_append_kv

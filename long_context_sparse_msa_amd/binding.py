@@ -30,7 +30,8 @@ MSA_DTYPE_BF16 = 1
 EXPORTS = (
     "msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
     "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_status_string",
-    "msa_last_error", "msa_abi_version",
+    "msa_last_error", "msa_abi_version", "msa_decode_fwd_varlen", "msa_append_kv",
+    "msa_plan_decode_varlen",
 )
 
 
@@ -74,8 +75,12 @@ def lib() -> ctypes.CDLL:
         L.msa_plan_rows.argtypes = [P(AttnDesc), vp, vp]
         L.msa_plan_tiles.argtypes = [P(AttnDesc), vp, i64, P(i64), P(i32), P(i32)]
         L.msa_plan_decode.argtypes = [P(DecodeDesc), vp, P(i32), P(i32)]
+        L.msa_decode_fwd_varlen.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.msa_append_kv.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+        L.msa_plan_decode_varlen.argtypes = [P(DecodeDesc), i32, vp, P(i32), P(i32)]
         for f in ("msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
-                  "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode"):
+                  "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_decode_fwd_varlen",
+                  "msa_append_kv", "msa_plan_decode_varlen"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -218,6 +223,54 @@ def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_s
     return O, LSE
 
 
+def msa_decode_fwd_varlen(q, Kc, Vc, Kbar, Vbar, ctx_lens, window: int, num_landmarks: int,
+                          num_splits: int, scale: Optional[float] = None, out_dtype=None, workspace=None,
+                          O=None, LSE=None, want_lse: bool = True, stream=None):
+    """Decode of sequences of different lengths: sequence b holds
+    ctx_lens[b] tokens (int32 device tensor [B]) of a cache with capacity
+    Kc.shape[2] rows; its query is at position ctx_lens[b]-1.  Landmark
+    blocks have length capacity / num_landmarks.  (O [B][Hq][d], LSE [B][Hq])."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, cap = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, cap, d) or Vc.shape != Kc.shape:
+        raise ValueError("cache shapes do not match q")
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code)
+    need = msa_decode_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=_torch_dtype(out_code), device=q.device)
+    if LSE is None and want_lse:
+        LSE = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib().msa_decode_fwd_varlen(ctypes.byref(desc), _ptr(ctx_lens), _ptr(q), _ptr(Kc), _ptr(Vc),
+                                       _ptr(Kbar), _ptr(Vbar), _ptr(workspace), ws_bytes, _ptr(O), _ptr(LSE),
+                                       _stream(q, stream)))
+    return O, LSE
+
+
+def msa_append_kv(k_new, v_new, positions, Kc, Vc, Kbar, Vbar, num_landmarks: int, stream=None):
+    """Store one token per sequence (k_new, v_new [B][Hkv][d]) at row
+    positions[b] (int32 device tensor [B]; outside [0, capacity) = skip) of
+    the caches, in place, and re-pool the landmark block that row completes."""
+    import torch
+    B, Hkv, cap, d = Kc.shape
+    if Vc.shape != Kc.shape or tuple(k_new.shape) != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new [B][Hkv][d] must match the caches [B][Hkv][C][d]")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (B,):
+        raise ValueError("positions must be an int32 tensor of shape [B]")
+    if k_new.dtype != Kc.dtype or v_new.dtype != Kc.dtype or Vc.dtype != Kc.dtype:
+        raise ValueError("new rows and caches must share a dtype")
+    desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kc.dtype))
+    _check(lib().msa_append_kv(ctypes.byref(desc), _ptr(positions), _ptr(k_new), _ptr(v_new), _ptr(Kc),
+                               _ptr(Vc), _ptr(Kbar), _ptr(Vbar), _stream(Kc, stream)))
+
+
 def decode_partials(workspace, num_splits: int, batch: int, heads_q: int, head_dim: int):
     """Views of the per-chunk results held in a decode workspace:
     (o [S][B][Hq][d], lse [S][B][Hq]), both float32."""
@@ -257,6 +310,17 @@ def msa_plan_decode(desc: DecodeDesc):
     lm = ctypes.c_int32(0)
     ent = ctypes.c_int32(0)
     _check(lib().msa_plan_decode(ctypes.byref(desc), bounds.ctypes.data, ctypes.byref(lm), ctypes.byref(ent)))
+    return bounds, lm.value, ent.value
+
+
+def msa_plan_decode_varlen(desc: DecodeDesc, ctx: int):
+    """Plan of one sequence of ctx tokens in a cache of capacity
+    desc.ctx_len: (chunk_bounds int32 [S+1], visible landmarks, entries)."""
+    bounds = np.zeros(desc.num_splits + 1, dtype=np.int32)
+    lm = ctypes.c_int32(0)
+    ent = ctypes.c_int32(0)
+    _check(lib().msa_plan_decode_varlen(ctypes.byref(desc), int(ctx), bounds.ctypes.data, ctypes.byref(lm),
+                                        ctypes.byref(ent)))
     return bounds, lm.value, ent.value
 
 

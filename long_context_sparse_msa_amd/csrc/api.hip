@@ -191,9 +191,64 @@ msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void
     return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
-  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, ws_o, ws_lse, O, LSE,
+  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, nullptr, ws_o, ws_lse, O, LSE,
                                        static_cast<hipStream_t>(stream)),
                     "decode launch");
+}
+
+msa_status msa_decode_fwd_varlen(const msa_decode_desc* desc, const int32_t* ctx_lens, const void* q,
+                                 const void* Kcache, const void* Vcache, const void* Kbar, const void* Vbar,
+                                 void* workspace, size_t workspace_bytes, void* O, float* LSE, void* stream) {
+  msa_status s = check_decode(desc);
+  if (s != MSA_OK) return s;
+  if (desc->batch == 0) return ok();
+  if (ctx_lens == nullptr) return fail(MSA_ERR_INVALID_ARG, "ctx_lens is NULL");
+  if ((reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "ctx_lens is not 4-byte aligned");
+  if ((s = check_ptr(q, "q")) || (s = check_ptr(Kcache, "Kcache")) || (s = check_ptr(Vcache, "Vcache")) ||
+      (s = check_ptr(O, "O")) || (s = check_ptr(workspace, "workspace")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  if (LSE != nullptr && !aligned16(LSE)) return fail(MSA_ERR_INVALID_ARG, "LSE is not 16-byte aligned");
+  const size_t need = decode_ws_bytes(desc);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
+  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, ctx_lens, ws_o, ws_lse, O, LSE,
+                                       static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+msa_status msa_append_kv(const msa_decode_desc* desc, const int32_t* positions, const void* k_new,
+                         const void* v_new, void* Kcache, void* Vcache, void* Kbar, void* Vbar, void* stream) {
+  if (desc == nullptr) return fail(MSA_ERR_INVALID_ARG, "desc is NULL");
+  if (desc->batch < 0 || desc->ctx_len < 1 || desc->heads_kv < 1)
+    return fail(MSA_ERR_INVALID_ARG, "batch=%d ctx_len=%d heads_kv=%d: need batch>=0, ctx_len>=1, heads_kv>=1",
+                desc->batch, desc->ctx_len, desc->heads_kv);
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim=%d: supported values are 64 and 128", desc->head_dim);
+  if (desc->num_landmarks < 0 || (desc->num_landmarks > 0 && desc->ctx_len % desc->num_landmarks != 0))
+    return fail(MSA_ERR_INVALID_ARG, "num_landmarks=%d must be >= 0 and divide ctx_len=%d", desc->num_landmarks,
+                desc->ctx_len);
+  if (desc->in_dtype != MSA_DTYPE_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "the cache is bf16 only (in_dtype=%d)", desc->in_dtype);
+  if ((long long)desc->ctx_len * desc->head_dim * 2 >= (1LL << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "ctx_len=%d: one head's cache must be < 2 GiB", desc->ctx_len);
+  if (2LL * desc->batch * desc->heads_kv > (1LL << 31) - 1)
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (desc->batch == 0) return ok();
+  if (positions == nullptr) return fail(MSA_ERR_INVALID_ARG, "positions is NULL");
+  if ((reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "positions is not 4-byte aligned");
+  msa_status s;
+  if ((s = check_ptr(k_new, "k_new")) || (s = check_ptr(v_new, "v_new")) || (s = check_ptr(Kcache, "Kcache")) ||
+      (s = check_ptr(Vcache, "Vcache")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  return hip_status(msa::launch_append(*desc, positions, k_new, v_new, Kcache, Vcache, Kbar, Vbar,
+                                       static_cast<hipStream_t>(stream)),
+                    "append launch");
 }
 
 msa_status msa_plan_rows(const msa_attn_desc* desc, int32_t* win_lo, int32_t* lm_count) {
@@ -257,6 +312,26 @@ msa_status msa_plan_decode(const msa_decode_desc* desc, int32_t* chunk_bounds, i
   if (chunk_bounds == nullptr || lm_visible == nullptr || entries == nullptr)
     return fail(MSA_ERR_INVALID_ARG, "output is NULL");
   const msa::DecodePlan p = msa::decode_plan(desc->ctx_len, desc->window, desc->num_landmarks, desc->num_splits);
+  for (int c = 0; c <= desc->num_splits; ++c) {
+    const long long b = (long long)c * p.chunk;
+    chunk_bounds[c] = (int32_t)(b < p.entries ? b : p.entries);
+  }
+  *lm_visible = p.lm;
+  *entries = p.entries;
+  return ok();
+}
+
+msa_status msa_plan_decode_varlen(const msa_decode_desc* desc, int32_t ctx, int32_t* chunk_bounds,
+                                  int32_t* lm_visible, int32_t* entries) {
+  msa_status s = check_decode(desc);
+  if (s != MSA_OK) return s;
+  if (ctx < 0 || ctx > desc->ctx_len)
+    return fail(MSA_ERR_INVALID_ARG, "ctx=%d outside [0, ctx_len=%d]", ctx, desc->ctx_len);
+  if (chunk_bounds == nullptr || lm_visible == nullptr || entries == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "output is NULL");
+  const int G = desc->num_landmarks;
+  const msa::DecodePlan p =
+      msa::decode_plan_fixed(ctx, desc->window, G, G > 0 ? desc->ctx_len / G : 1, desc->num_splits);
   for (int c = 0; c <= desc->num_splits; ++c) {
     const long long b = (long long)c * p.chunk;
     chunk_bounds[c] = (int32_t)(b < p.entries ? b : p.entries);

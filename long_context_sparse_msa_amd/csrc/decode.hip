@@ -273,13 +273,32 @@ struct DecodeArgs {
   float *ws_o, *ws_lse;
   void* Out;
   float* LSE;
-  int B, Hq, Hkv, ctx, G;
-  float c2;  // scale * log2(e)
-  int lm, win0, E, chunk, S;
+  int B, Hq, Hkv, ctx, G;  // ctx: cache rows per (sequence, KV head); G: landmark slots
+  float c2;                // scale * log2(e)
+  int lm, win0, E, chunk, S;  // plan of row ctx-1 (used when lens is null)
+  const int32_t* lens;     // per-sequence lengths, or null: every sequence holds ctx tokens
+  int w, L;                // window and landmark block length (lens path)
 };
 
+// Plan of sequence b: the static one, or that of its own length (clamped to
+// [0, ctx]; 0 gives an empty list).
+__device__ __forceinline__ DecodePlan seq_plan(const DecodeArgs& A, int b) {
+  if (A.lens == nullptr) {
+    DecodePlan p;
+    p.lm = A.lm;
+    p.win0 = A.win0;
+    p.entries = A.E;
+    p.chunk = A.chunk;
+    p.win = A.E - A.lm;
+    return p;
+  }
+  int n = A.lens[b];
+  n = n < 0 ? 0 : (n > A.ctx ? A.ctx : n);
+  return decode_plan_fixed(n, A.w, A.G, A.L, A.S);
+}
+
 template <int D, int TE>
-__device__ __forceinline__ Stager<D, TE> make_stager(const DecodeArgs& A, int bk, int lane) {
+__device__ __forceinline__ Stager<D, TE> make_stager(const DecodeArgs& A, int bk, int lane, const DecodePlan& p) {
   const unsigned char* kc = reinterpret_cast<const unsigned char*>(A.Kc + (size_t)bk * A.ctx * D);
   const unsigned char* vc = reinterpret_cast<const unsigned char*>(A.Vc + (size_t)bk * A.ctx * D);
   const unsigned char* kl = kc;
@@ -288,7 +307,7 @@ __device__ __forceinline__ Stager<D, TE> make_stager(const DecodeArgs& A, int bk
     kl = reinterpret_cast<const unsigned char*>(A.Kb + (size_t)bk * A.G * D);
     vl = reinterpret_cast<const unsigned char*>(A.Vb + (size_t)bk * A.G * D);
   }
-  return Stager<D, TE>{kl, vl, kc, vc, A.lm, A.win0, lane};
+  return Stager<D, TE>{kl, vl, kc, vc, p.lm, p.win0, lane};
 }
 
 // ---------------------------------------------------------------------------
@@ -303,10 +322,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs A) {
   const int grp = A.Hq / A.Hkv;
   const int lane = threadIdx.x, c16 = lane & 15, g4 = lane >> 4;
 
-  const int e_beg = c * A.chunk;
-  const int e_end = min(A.E, e_beg + A.chunk);
+  const DecodePlan p = seq_plan(A, b);
+  const int e_beg = c * p.chunk;
+  const int e_end = min(p.entries, e_beg + p.chunk);
   const int n_t = e_end > e_beg ? (e_end - e_beg + TE - 1) / TE : 0;
-  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane);
+  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane, p);
   WaveOps<D, TE> w;
   w.init(A.q + ((size_t)b * A.Hq + kvh * grp) * D, grp, c16, g4);
   Acc<D> a;
@@ -344,13 +364,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_fused_kernel(DecodeAr
   unsigned char* ring = smem + wave * T::RING;
 
   // chunks of this wavefront; chunk c is non-empty iff c * chunk < E
+  const DecodePlan p = seq_plan(A, b);
   const int c0 = wave * A.S / kFusedWaves;
   const int c1 = (wave + 1) * A.S / kFusedWaves;
-  const int n_ne = (A.E + A.chunk - 1) / A.chunk;
+  const int n_ne = p.chunk > 0 ? (p.entries + p.chunk - 1) / p.chunk : 0;
   const int cend = min(c1, n_ne);
-  const ChunkTiles<TE> ct{A.chunk, A.E};
+  const ChunkTiles<TE> ct{p.chunk, p.entries};
 
-  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane);
+  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane, p);
   WaveOps<D, TE> w;
   w.init(A.q + ((size_t)b * A.Hq + kvh * grp) * D, grp, c16, g4);
 
@@ -473,7 +494,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) tot += __shfl_xor(tot, sh);
-  const float inv = 1.0f / tot;
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;  // every chunk empty: O = 0, LSE = -inf
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const float val = acc[e] * inv;
@@ -483,7 +504,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
       static_cast<float*>(Out)[(size_t)bh * D + lane + 64 * e] = val;
     }
   }
-  if (LSE != nullptr && lane == 0) LSE[bh] = M + logf(tot);
+  if (LSE != nullptr && lane == 0) LSE[bh] = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
 
 // Compute units of the current device (cached per device).
@@ -511,13 +532,14 @@ bool use_fused(const msa_decode_desc& d) {
 
 template <int D>
 hipError_t launch_t(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                    const void* Kb, const void* Vb, float* ws_o, float* ws_lse, void* O, float* LSE,
-                    hipStream_t stream) {
+                    const void* Kb, const void* Vb, const int32_t* lens, float* ws_o, float* ws_lse, void* O,
+                    float* LSE, hipStream_t stream) {
   const DecodePlan p = decode_plan(d.ctx_len, d.window, d.num_landmarks, d.num_splits);
+  const int L = d.num_landmarks > 0 ? d.ctx_len / d.num_landmarks : 1;
   DecodeArgs A{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(Kc), static_cast<const uint16_t*>(Vc),
                static_cast<const uint16_t*>(Kb), static_cast<const uint16_t*>(Vb), ws_o, ws_lse, O, LSE,
                d.batch, d.heads_q, d.heads_kv, d.ctx_len, d.num_landmarks, d.scale * kLog2e, p.lm, p.win0,
-               p.entries, p.chunk, d.num_splits};
+               p.entries, p.chunk, d.num_splits, lens, d.window, L};
   const long long pairs = (long long)d.batch * d.heads_kv;
   if (use_fused(d)) {
     if (d.out_dtype == MSA_DTYPE_BF16) {
@@ -547,10 +569,10 @@ hipError_t launch_t(const msa_decode_desc& d, const void* q, const void* Kc, con
 }  // namespace
 
 hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                         const void* Kbar, const void* Vbar, float* ws_o, float* ws_lse, void* O,
-                         float* LSE, hipStream_t stream) {
-  return d.head_dim == 128 ? launch_t<128>(d, q, Kc, Vc, Kbar, Vbar, ws_o, ws_lse, O, LSE, stream)
-                           : launch_t<64>(d, q, Kc, Vc, Kbar, Vbar, ws_o, ws_lse, O, LSE, stream);
+                         const void* Kbar, const void* Vbar, const int32_t* lens, float* ws_o, float* ws_lse,
+                         void* O, float* LSE, hipStream_t stream) {
+  return d.head_dim == 128 ? launch_t<128>(d, q, Kc, Vc, Kbar, Vbar, lens, ws_o, ws_lse, O, LSE, stream)
+                           : launch_t<64>(d, q, Kc, Vc, Kbar, Vbar, lens, ws_o, ws_lse, O, LSE, stream);
 }
 
 }  // namespace msa

@@ -19,8 +19,14 @@ hipError_t launch_attn_f32(const msa_attn_desc& d, const void* Q, const void* K,
                            const void* Kbar, const void* Vbar, void* O, float* LSE,
                            hipStream_t stream);
 
+// lens: per-sequence lengths in device memory, or null for ctx_len each.
 hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                         const void* Kbar, const void* Vbar, float* ws_o, float* ws_lse, void* O,
-                         float* LSE, hipStream_t stream);
+                         const void* Kbar, const void* Vbar, const int32_t* lens, float* ws_o, float* ws_lse,
+                         void* O, float* LSE, hipStream_t stream);
+
+// Write one token's K/V row per sequence at positions[b] (skipped outside
+// [0, ctx_len)) and re-pool the landmark block that row completes.
+hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
+                         const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar, hipStream_t stream);
 
 }  // namespace msa

@@ -77,16 +77,26 @@ struct DecodePlan {
   int chunk;    // entries per chunk, ceil(entries / S)
 };
 
-__host__ __device__ inline DecodePlan decode_plan(int ctx, int w, int G, int S) {
+// Row n-1 of a sequence of n >= 0 tokens whose landmark blocks have length
+// L (G blocks of capacity).  n = 0 gives an empty list (chunk 0).
+__host__ __device__ inline DecodePlan decode_plan_fixed(int n, int w, int G, int L, int S) {
   DecodePlan p;
-  const int L = G > 0 ? ctx / G : 1;
-  const int i = ctx - 1;
+  if (n <= 0) {
+    p.lm = p.win = p.win0 = p.entries = p.chunk = 0;
+    return p;
+  }
+  const int i = n - 1;
   p.lm = lm_count(i, w, G, L);
   p.win0 = win_lo(i, w);
   p.win = i - p.win0 + 1;
   p.entries = p.lm + p.win;
   p.chunk = (p.entries + S - 1) / S;
   return p;
+}
+
+// Static decode: the whole cache of ctx tokens, L = ctx / G.
+__host__ __device__ inline DecodePlan decode_plan(int ctx, int w, int G, int S) {
+  return decode_plan_fixed(ctx, w, G, G > 0 ? ctx / G : 1, S);
 }
 
 }  // namespace msa

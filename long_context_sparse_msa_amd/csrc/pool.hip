@@ -4,6 +4,11 @@
 // Game", taken as block means).  Pure streaming: every input byte is read
 // once with 16-byte loads; float32 accumulation in a fixed order, so the
 // result is deterministic; round-to-nearest-even into the input dtype.
+//
+// Append (incremental decode): one new K/V row per sequence is stored and,
+// when it completes a landmark block, that block is pooled again by the
+// same code, so a cache filled token by token holds the same landmark bits
+// as one pooled at once.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -43,27 +48,25 @@ struct Chunk<float> {
   }
 };
 
-// One workgroup per (tensor, batch*kv_head, landmark).  Threads are laid
-// out as kRowLanes row lanes x kChunks 16-byte column chunks; row lane rl
-// sums rows rl, rl + kRowLanes, ... of the block, then the row lanes are
-// added in order through LDS.
+// Mean of the L rows of one block (row stride D elements) by one workgroup
+// of 256 threads, laid out as kRowLanes row lanes x kChunks 16-byte column
+// chunks: row lane rl sums rows rl, rl + kRowLanes, ... of the block in
+// ascending order, then the row lanes are added in order through LDS and
+// the sum divided by L.  With LAST, row L-1 is read from `last` instead of
+// the block (the row an append is writing), which gives the same bits as
+// pooling the block once that row is stored.  Called by every thread.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, const T* __restrict__ V,
-                                                   T* __restrict__ Kbar, T* __restrict__ Vbar, int n,
-                                                   int G, int L, int blocks_per_tensor) {
-  constexpr int kE = Chunk<T>::kElems;
-  constexpr int kChunks = D / kE;
-  constexpr int kRowLanes = 256 / kChunks;
-  __shared__ float red[kRowLanes][D + 1];
+struct PoolShape {
+  static constexpr int kE = Chunk<T>::kElems;
+  static constexpr int kChunks = D / kE;
+  static constexpr int kRowLanes = 256 / kChunks;
+};
 
-  const int wg = blockIdx.x;
-  const bool is_v = wg >= blocks_per_tensor;
-  const int blk = is_v ? wg - blocks_per_tensor : wg;  // over batch*kv_heads*G
-  const int bh = blk / G;
-  const int lm = blk - bh * G;
-  const T* src = (is_v ? V : K) + ((size_t)bh * n + (size_t)lm * L) * D;
-  T* dst = (is_v ? Vbar : Kbar) + (size_t)blk * D;
-
+template <typename T, int D, bool LAST>
+__device__ __forceinline__ void pool_block(const T* __restrict__ src, const T* __restrict__ last, int L,
+                                           T* __restrict__ dst, float (*red)[D + 1]) {
+  using PS = PoolShape<T, D>;
+  constexpr int kE = PS::kE, kChunks = PS::kChunks, kRowLanes = PS::kRowLanes;
   const int ch = threadIdx.x % kChunks;
   const int rl = threadIdx.x / kChunks;
   float acc[kE];
@@ -71,19 +74,21 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, cons
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
 
   const u32x4* p = reinterpret_cast<const u32x4*>(src) + ch;
+  const u32x4* lp = reinterpret_cast<const u32x4*>(last) + ch;
   constexpr int kStride = kChunks;  // u32x4 per row
+  auto row = [&](int r) -> const u32x4* { return (LAST && r == L - 1) ? lp : p + (size_t)r * kStride; };
   int r = rl;
   for (; r + 3 * kRowLanes < L; r += 4 * kRowLanes) {
-    const u32x4 a = p[(size_t)r * kStride];
-    const u32x4 b = p[(size_t)(r + kRowLanes) * kStride];
-    const u32x4 c = p[(size_t)(r + 2 * kRowLanes) * kStride];
-    const u32x4 d = p[(size_t)(r + 3 * kRowLanes) * kStride];
+    const u32x4 a = *row(r);
+    const u32x4 b = *row(r + kRowLanes);
+    const u32x4 c = *row(r + 2 * kRowLanes);
+    const u32x4 d = *row(r + 3 * kRowLanes);
     Chunk<T>::add(acc, a);
     Chunk<T>::add(acc, b);
     Chunk<T>::add(acc, c);
     Chunk<T>::add(acc, d);
   }
-  for (; r < L; r += kRowLanes) Chunk<T>::add(acc, p[(size_t)r * kStride]);
+  for (; r < L; r += kRowLanes) Chunk<T>::add(acc, *row(r));
 
 #pragma unroll
   for (int e = 0; e < kE; ++e) red[rl][ch * kE + e] = acc[e];
@@ -100,6 +105,52 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, cons
   }
 }
 
+// One workgroup per (tensor, batch*kv_head, landmark).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, const T* __restrict__ V,
+                                                   T* __restrict__ Kbar, T* __restrict__ Vbar, int n,
+                                                   int G, int L, int blocks_per_tensor) {
+  __shared__ float red[PoolShape<T, D>::kRowLanes][D + 1];
+  const int wg = blockIdx.x;
+  const bool is_v = wg >= blocks_per_tensor;
+  const int blk = is_v ? wg - blocks_per_tensor : wg;  // over batch*kv_heads*G
+  const int bh = blk / G;
+  const int lm = blk - bh * G;
+  const T* src = (is_v ? V : K) + ((size_t)bh * n + (size_t)lm * L) * D;
+  T* dst = (is_v ? Vbar : Kbar) + (size_t)blk * D;
+  pool_block<T, D, false>(src, nullptr, L, dst, red);
+}
+
+// Append: one workgroup per (tensor, batch*kv_head).  The sequence's new
+// row goes to position pos of its cache; if it is the last row of block
+// blk = (pos+1)/L - 1, that block's landmark is pooled again (rows before
+// pos from the cache, row pos from the new token).  A position outside
+// [0, C) leaves the sequence untouched.
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(const int32_t* __restrict__ positions,
+                                                     const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ Kc,
+                                                     uint16_t* __restrict__ Vc, uint16_t* __restrict__ Kbar,
+                                                     uint16_t* __restrict__ Vbar, int Hkv, int C, int G, int L,
+                                                     int pairs) {
+  __shared__ float red[PoolShape<uint16_t, D>::kRowLanes][D + 1];
+  const int wg = blockIdx.x;
+  const bool is_v = wg >= pairs;
+  const int bk = is_v ? wg - pairs : wg;  // b * Hkv + kvh
+  const int pos = positions[bk / Hkv];
+  if (pos < 0 || pos >= C) return;
+  const uint16_t* src = (is_v ? v_new : k_new) + (size_t)bk * D;
+  uint16_t* cache = (is_v ? Vc : Kc) + (size_t)bk * C * D;
+  if (threadIdx.x < D / 8) {
+    reinterpret_cast<u32x4*>(cache + (size_t)pos * D)[threadIdx.x] = reinterpret_cast<const u32x4*>(src)[threadIdx.x];
+  }
+  if (G > 0 && (pos + 1) % L == 0) {
+    const int blk = (pos + 1) / L - 1;
+    uint16_t* dst = (is_v ? Vbar : Kbar) + ((size_t)bk * G + blk) * D;
+    pool_block<uint16_t, D, true>(cache + (size_t)blk * L * D, src, L, dst, red);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_pool_t(const msa_attn_desc& d, const void* K, const void* V, void* Kb, void* Vb,
                          hipStream_t stream) {
@@ -112,7 +163,26 @@ hipError_t launch_pool_t(const msa_attn_desc& d, const void* K, const void* V, v
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_append_t(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
+                           const void* v_new, void* Kc, void* Vc, void* Kb, void* Vb, hipStream_t stream) {
+  const int G = d.num_landmarks;
+  const int L = G > 0 ? d.ctx_len / G : 1;
+  const int pairs = d.batch * d.heads_kv;
+  hipLaunchKernelGGL((append_kernel<D>), dim3(2 * pairs), dim3(256), 0, stream, positions,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     static_cast<uint16_t*>(Kc), static_cast<uint16_t*>(Vc), static_cast<uint16_t*>(Kb),
+                     static_cast<uint16_t*>(Vb), d.heads_kv, d.ctx_len, G, L, pairs);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
+                         const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar, hipStream_t stream) {
+  return d.head_dim == 128 ? launch_append_t<128>(d, positions, k_new, v_new, Kc, Vc, Kbar, Vbar, stream)
+                           : launch_append_t<64>(d, positions, k_new, v_new, Kc, Vc, Kbar, Vbar, stream);
+}
 
 hipError_t launch_pool(const msa_attn_desc& d, const void* K, const void* V, void* Kbar, void* Vbar,
                        hipStream_t stream) {

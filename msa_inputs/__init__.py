@@ -168,6 +168,15 @@ def device_decode_inputs(cfg: Decode, device, seed: int = SEED_PLAIN):
     return q, kc, vc
 
 
+def decode_lengths(batch: int, capacity: int, seed: int = SEED_PLAIN, lo_frac: float = 0.5) -> np.ndarray:
+    """Seeded per-sequence context lengths for incremental decode: uniform
+    integers in [lo_frac * capacity, capacity] (a batch of long documents at
+    different points of their generation).  int32 [batch]."""
+    rng = np.random.default_rng(1000 + seed)
+    lo = max(1, int(lo_frac * capacity))
+    return rng.integers(lo, capacity + 1, size=batch).astype(np.int32)
+
+
 def sample_rows(n: int, head: int, count: int = 4096, window: int = 0, block: int = 0) -> np.ndarray:
     """Seeded sample of query rows for one head (generator seeded 12345+head),
     plus forced edge rows around the start, the window edge, the first

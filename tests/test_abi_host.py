@@ -31,14 +31,14 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 13
     assert sorted(msa.EXPORTS) == names
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version(L):
-    assert msa.abi_version() == 1
+    assert msa.abi_version() == 2
 
 
 def test_status_strings(L):
@@ -194,3 +194,74 @@ def test_plan_decode_bitexact(ctx, w, G, S):
     assert ent == len(idx)
     assert lm == int((kinds == 0).sum())
     np.testing.assert_array_equal(bounds, orc.chunk_bounds(len(idx), S))
+
+
+# ---------------------------------------------------------- incremental decode
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_splits=0), 1), (dict(window=0), 1), (dict(num_landmarks=7), 1), (dict(ctx_len=0), 1),
+    (dict(heads_q=40, heads_kv=2), 2), (dict(head_dim=96), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32), 2), (dict(ctx_len=1 << 23), 2),
+])
+def test_decode_varlen_validation(kw, status):
+    d = dec_desc(**kw)
+    p = ctypes.c_void_p(16)
+    assert msa.lib().msa_decode_fwd_varlen(ctypes.byref(d), p, p, p, p, p, p, p, 1 << 30, p, None, None) == status
+
+
+def test_decode_varlen_pointer_checks():
+    d = dec_desc()
+    p = ctypes.c_void_p(16)
+    f = msa.lib().msa_decode_fwd_varlen
+    assert f(ctypes.byref(d), None, p, p, p, p, p, p, 1 << 30, p, None, None) == 1
+    assert b"ctx_lens" in msa.lib().msa_last_error()
+    assert f(ctypes.byref(d), ctypes.c_void_p(18), p, p, p, p, p, p, 1 << 30, p, None, None) == 1
+    assert f(ctypes.byref(d), ctypes.c_void_p(20), p, p, p, p, p, p, 16, p, None, None) == 3
+    d0 = dec_desc(batch=0)
+    assert f(ctypes.byref(d0), None, None, None, None, None, None, None, 0, None, None, None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ctx_len=0), 1), (dict(heads_kv=0), 1), (dict(num_landmarks=7), 1), (dict(head_dim=96), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32), 2), (dict(ctx_len=1 << 23), 2),
+])
+def test_append_validation(kw, status):
+    d = dec_desc(**kw)
+    p = ctypes.c_void_p(16)
+    assert msa.lib().msa_append_kv(ctypes.byref(d), p, p, p, p, p, p, p, None) == status
+
+
+def test_append_pointer_checks():
+    d = dec_desc()
+    p = ctypes.c_void_p(16)
+    f = msa.lib().msa_append_kv
+    assert f(ctypes.byref(d), None, p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), ctypes.c_void_p(18), p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), p, ctypes.c_void_p(24), p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), p, p, p, p, p, None, p, None) == 1
+    assert b"Kbar" in msa.lib().msa_last_error()
+    d0 = dec_desc(batch=0)
+    assert f(ctypes.byref(d0), None, None, None, None, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("C,w,G,S", [(524288, 4096, 512, 16), (512, 64, 8, 4), (100, 1000, 0, 3),
+                                      (64, 8, 8, 40), (4096, 300, 16, 7)])
+def test_plan_decode_varlen_bitexact(C, w, G, S):
+    d = dec_desc(ctx_len=C, window=w, num_landmarks=G, num_splits=S)
+    L = C // G if G else 1
+    rng = np.random.default_rng(C + w)
+    lens = sorted({0, 1, 2, C, C - 1, w, w + 1} | set(rng.integers(0, C + 1, 25).tolist()))
+    for n in lens:
+        if n > C:
+            continue
+        bounds, lm, ent = msa.msa_plan_decode_varlen(d, n)
+        kinds, idx = orc.visible_list_fixed(n - 1, w, L, G) if n else (np.zeros(0), np.zeros(0))
+        assert ent == len(idx), n
+        assert lm == int((kinds == 0).sum()), n
+        np.testing.assert_array_equal(bounds, orc.chunk_bounds(len(idx), S))
+    with pytest.raises(msa.MsaError):
+        msa.msa_plan_decode_varlen(d, C + 1)
+    with pytest.raises(msa.MsaError):
+        msa.msa_plan_decode_varlen(d, -1)
+    # the full length is the static plan
+    np.testing.assert_array_equal(msa.msa_plan_decode_varlen(d, C)[0], msa.msa_plan_decode(d)[0])

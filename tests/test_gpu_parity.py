@@ -313,6 +313,16 @@ def dec512k():
         os.environ.pop("MSA_DECODE_SCHEDULE", None)
     po, pl = msa.decode_partials(ws, cfg.num_splits, cfg.batch, cfg.heads_q, cfg.head_dim)
     r["po"], r["pl"] = host64(po[:, 0]), host64(pl[:, 0])
+    # the same caches holding sequences of different lengths (incremental decode)
+    r["lens"] = wl.decode_lengths(cfg.batch, cfg.ctx_len)
+    lens_d = torch.from_numpy(r["lens"]).to(dev())
+    r["Ov"], r["Lv"] = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, *args[5:], out_dtype=torch.float32)
+    os.environ["MSA_DECODE_SCHEDULE"] = "split"
+    try:
+        r["Ovs"], r["Lvs"] = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, *args[5:],
+                                                       out_dtype=torch.float32, workspace=ws)
+    finally:
+        os.environ.pop("MSA_DECODE_SCHEDULE", None)
     torch.cuda.synchronize()
     del Kb, Vb, ws
     yield r
@@ -336,6 +346,12 @@ def test_decode_workload_512k(dec512k, b):
                  f"{cfg.name} seq {b} (64 heads)")
     assert_close(host64(r["Os"][b:b + 1]), host64(r["Ls"][b:b + 1]), o_ref, l_ref, TOL_BF16,
                  f"{cfg.name} seq {b} (64 heads), split schedule")
+    n = int(r["lens"][b])
+    L = cfg.ctx_len // cfg.num_landmarks
+    ov, lv = orc.decode_varlen(q64, k64, v64, [n], cfg.window, L, cfg.num_landmarks, cfg.scale)
+    for key, sched in (("", "fused"), ("s", "split")):
+        assert_close(host64(r["Ov" + key][b:b + 1]), host64(r["Lv" + key][b:b + 1]), ov, lv, TOL_BF16,
+                     f"{cfg.name} seq {b} at length {n} (64 heads), {sched} schedule")
     if b == 0:
         kb_r = host64(torch.from_numpy(orc.pool(k64, cfg.num_landmarks)).to(torch.bfloat16))
         vb_r = host64(torch.from_numpy(orc.pool(v64, cfg.num_landmarks)).to(torch.bfloat16))
