@@ -42,6 +42,12 @@ Readings taken where the pages leave the step open:
   always a complete block.  With every length equal to the capacity this is
   the decode above.  A sequence of length 0 has O = 0 and LSE = -inf.
 
+* Backward: the gradients of O with respect to Q, K and V for an upstream
+  dO are the chain rule through the same single softmax; a landmark is the
+  mean of its block, so each row of the block receives 1/L of the
+  landmark's gradient.  The pages train at these lengths but do not write
+  the backward out.
+
 Every predicate below is evaluated by explicit comparisons; nothing uses a
 closed-form count of visible keys.
 """
@@ -486,3 +492,137 @@ def append_tokens(Kc, Vc, Kbar, Vbar, positions, k_new, v_new, L: int):
             blk = (pos + 1) // L - 1
             Kbar[b, :, blk] = Kc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
             Vbar[b, :, blk] = Vc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Step 8: backward -- gradients of O with respect to Q, K and V for a given
+# upstream gradient dO.  The pages train at these lengths ("Training at 1M+
+# Token Context ...", Flash Attention and Block-Sparse Flash Attention
+# paragraphs; "Million Token Context Window Optimization ...", section
+# "Distributed training"), without writing the backward out; what follows is
+# the chain rule applied to the forward above, nothing more:
+#   P = softmax over the visible entries,  O = P V_vis
+#   dP = dO V_vis^T,  D = rowsum(dO * O),  dS = P * (dP - D)
+#   dQ = scale dS K_vis,  dK_vis = scale dS^T Q,  dV_vis = P^T dO
+# summed over the query heads that share a KV head.  A landmark is the mean
+# of its block, so each of the block's L rows receives 1/L of the
+# landmark's gradient.
+# ---------------------------------------------------------------------------
+
+def _probs(S_win, M_win, S_lm, M_lm):
+    """Normalised probabilities of one softmax over the visible window and
+    landmark scores: (P_win, P_lm, LSE)."""
+    S_win = np.where(M_win, S_win, NEG_INF)
+    S_lm = np.where(M_lm, S_lm, NEG_INF)
+    m = np.maximum(S_win.max(axis=1, initial=NEG_INF), S_lm.max(axis=1, initial=NEG_INF))
+    P_win = np.where(M_win, np.exp(S_win - m[:, None]), 0.0)
+    P_lm = np.where(M_lm, np.exp(S_lm - m[:, None]), 0.0)
+    l = P_win.sum(axis=1) + P_lm.sum(axis=1)
+    return P_win / l[:, None], P_lm / l[:, None], m + np.log(l)
+
+
+def _softmax_bwd(P, dP, D):
+    """Gradient of the scores of one softmax row: P * (dP - D)."""
+    return P * (dP - D[:, None])
+
+
+def _mean_bwd(dXbar, L: int):
+    """Adjoint of block-mean pooling: [..., G, d] -> [..., G*L, d], every row
+    of block b gets dXbar[b] / L."""
+    return np.repeat(dXbar, L, axis=-2) / L
+
+
+def attn_bwd(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
+             kv_heads: Optional[Sequence[int]] = None, group_span: int = 512):
+    """Gradients (dQ [B, Hq, n, d], dK, dV [B, Hkv, n, d]) of the forward
+    above, fp64, with landmarks the means of K and V.  ``kv_heads`` limits the
+    work to those KV heads and their query heads (the other entries are
+    zero).  Rows are processed in groups of nearby rows whose key range
+    strictly contains their windows, as in attn()."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    L = block_len(n, G) if G else 0
+    Kbar = pool(K, G) if G else np.zeros((B, Hkv, 0, d))
+    Vbar = pool(V, G) if G else np.zeros((B, Hkv, 0, d))
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    dKbar = np.zeros_like(Kbar)
+    dVbar = np.zeros_like(Vbar)
+    gsel = set(range(Hkv) if kv_heads is None else kv_heads)
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        if g not in gsel:
+            continue
+        for grp_rows in _row_groups(np.arange(n), group_span):
+            lo = max(0, int(grp_rows[0]) - w)
+            hi = min(n, int(grp_rows[-1]) + 2)
+            M_win = window_visible(grp_rows[:, None], np.arange(lo, hi)[None, :], w)
+            M_lm = (landmark_visible(grp_rows[:, None], np.arange(G)[None, :], L, w) if G
+                    else np.zeros((len(grp_rows), 0), dtype=bool))
+            for b in range(B):
+                q = Q[b, h, grp_rows]
+                do = dO[b, h, grp_rows]
+                ks, vs = K[b, g, lo:hi], V[b, g, lo:hi]
+                kb, vb = Kbar[b, g], Vbar[b, g]
+                P_win, P_lm, _ = _probs(scale * (q @ ks.T), M_win, scale * (q @ kb.T), M_lm)
+                O = P_win @ vs + P_lm @ vb
+                D = (do * O).sum(axis=1)
+                dS_win = _softmax_bwd(P_win, do @ vs.T, D)
+                dS_lm = _softmax_bwd(P_lm, do @ vb.T, D)
+                dQ[b, h, grp_rows] = scale * (dS_win @ ks + dS_lm @ kb)
+                dK[b, g, lo:hi] += scale * (dS_win.T @ q)
+                dV[b, g, lo:hi] += P_win.T @ do
+                dKbar[b, g] += scale * (dS_lm.T @ q)
+                dVbar[b, g] += P_lm.T @ do
+    if G:
+        dK += _mean_bwd(dKbar, L)
+        dV += _mean_bwd(dVbar, L)
+    return dQ, dK, dV
+
+
+def attn_bwd_dq_rows(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
+                     rows: Optional[Dict[int, np.ndarray]] = None, group_span: int = 512):
+    """dQ on selected rows only (dQ of a row needs only that row's visible
+    entries): {head: (rows, dQ [B, R, d])}."""
+    Q = np.asarray(Q)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    L = block_len(n, G) if G else 0
+    out = {}
+    for h in sorted(rows):
+        g = kv_head(h, Hq, Hkv)
+        r_all = np.asarray(rows[h], dtype=np.int64)
+        res = np.empty((B, len(r_all), d))
+        kb_all = [pool(np.asarray(K[b, g], np.float64), G) if G else np.zeros((0, d)) for b in range(B)]
+        vb_all = [pool(np.asarray(V[b, g], np.float64), G) if G else np.zeros((0, d)) for b in range(B)]
+        pos = 0
+        for grp_rows in _row_groups(r_all, group_span):
+            lo = max(0, int(grp_rows[0]) - w)
+            hi = min(n, int(grp_rows[-1]) + 2)
+            M_win = window_visible(grp_rows[:, None], np.arange(lo, hi)[None, :], w)
+            M_lm = (landmark_visible(grp_rows[:, None], np.arange(G)[None, :], L, w) if G
+                    else np.zeros((len(grp_rows), 0), dtype=bool))
+            for b in range(B):
+                q = np.asarray(Q[b, h, grp_rows], np.float64)
+                do = np.asarray(dO[b, h, grp_rows], np.float64)
+                ks = np.asarray(K[b, g, lo:hi], np.float64)
+                vs = np.asarray(V[b, g, lo:hi], np.float64)
+                kb, vb = kb_all[b], vb_all[b]
+                P_win, P_lm, _ = _probs(scale * (q @ ks.T), M_win, scale * (q @ kb.T), M_lm)
+                O = P_win @ vs + P_lm @ vb
+                D = (do * O).sum(axis=1)
+                dS_win = _softmax_bwd(P_win, do @ vs.T, D)
+                dS_lm = _softmax_bwd(P_lm, do @ vb.T, D)
+                res[b, pos:pos + len(grp_rows)] = scale * (dS_win @ ks + dS_lm @ kb)
+            pos += len(grp_rows)
+        out[h] = (r_all, res)
+    return out

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import msa_oracle as orc
+from tests import test_oracle_backward as bwd
 from tests import test_oracle_incremental as inc
 from tests import test_oracle_pins as pins
 
@@ -77,6 +78,20 @@ def _append_at_block_start(Kc, Vc, Kbar, Vbar, positions, k_new, v_new, L):
                 Vbar[b, :, blk] = Vc[b, :, blk * L:(blk + 1) * L].mean(axis=1)
 
 
+def _softmax_bwd_no_rowsum(P, dP, D):          # drops the D term
+    return P * dP
+
+
+def _mean_bwd_no_divide(dXbar, L):              # forgets the 1/L of the mean
+    return np.repeat(dXbar, L, axis=-2)
+
+
+def _mean_bwd_last_row(dXbar, L):               # sends the whole gradient to the block's last row
+    out = np.zeros(dXbar.shape[:-2] + (dXbar.shape[-2] * L, dXbar.shape[-1]))
+    out[..., L - 1::L, :] = dXbar
+    return out
+
+
 MUTANTS = {
     "window_wide": ("window_visible", _window_wide),
     "window_no_self": ("window_visible", _window_no_self),
@@ -90,6 +105,9 @@ MUTANTS = {
     "varlen_query_past_end": ("visible_list_fixed", _varlen_query_past_end),
     "pool_prefix_sum": ("pool_prefix", _pool_prefix_sum),
     "append_at_block_start": ("append_tokens", _append_at_block_start),
+    "bwd_no_rowsum": ("_softmax_bwd", _softmax_bwd_no_rowsum),
+    "bwd_mean_no_divide": ("_mean_bwd", _mean_bwd_no_divide),
+    "bwd_mean_last_row": ("_mean_bwd", _mean_bwd_last_row),
 }
 
 PIN_SET = [
@@ -108,6 +126,8 @@ PIN_SET = [
     lambda: inc.test_varlen_window_covers_everything_is_textbook_causal(9),
     lambda: inc.test_append_builds_closed_form_landmarks(),
     lambda: inc.test_append_then_decode_equals_decode_of_the_whole_prefix(),
+    lambda: bwd.test_backward_matches_finite_differences(9, 4, 3),
+    lambda: bwd.test_one_token_landmarks_give_causal_backward(7),
 ]
 
 
