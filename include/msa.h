@@ -54,7 +54,8 @@ extern "C" {
 #endif
 
 /* 1: pooling, prefill, static decode and plans.  2: adds incremental
- * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen). */
+ * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen) and
+ * the backward (msa_attn_bwd_workspace_size, msa_attn_bwd). */
 #define MSA_ABI_VERSION 2
 
 typedef enum {
@@ -125,6 +126,37 @@ msa_status msa_pool_landmarks(const msa_attn_desc* desc, const void* K, const vo
  * Attention paragraph of "Training at 1M+ Token Context ...". */
 msa_status msa_attn_fwd(const msa_attn_desc* desc, const void* Q, const void* K, const void* V,
                         const void* Kbar, const void* Vbar, void* O, float* LSE, void* stream);
+
+/* ---- Backward of msa_attn_fwd.  The pages train at these lengths
+ * ("Training at 1M+ Token Context: Ring Attention, YaRN, NTK-Aware Scaling
+ * GPU Cost", Flash Attention and Block-Sparse Flash Attention paragraphs)
+ * but do not write the backward out; it is the chain rule through the
+ * operation defined at the top of this file:
+ *   P = exp(S - LSE) over the visible entries,  dP = dO V_vis^T,
+ *   D_i = sum_d dO_i O_i,  dS = P (dP - D),
+ *   dQ = scale dS K_vis,  dK_vis = scale dS^T Q,  dV_vis = P^T dO,
+ * summed over the query heads that share a KV head, and each landmark's
+ * gradient spread over the L rows of its block with weight 1/L (the
+ * landmark is their mean).  dK, dV are the total gradients of K, V through
+ * both the window and the landmark paths. ---- */
+
+/* Bytes of device workspace msa_attn_bwd needs for `desc`.  Host only. */
+msa_status msa_attn_bwd_workspace_size(const msa_attn_desc* desc, size_t* bytes);
+
+/* Gradients of the prefill.  Inputs: Q, K, V, Kbar, Vbar as given to
+ * msa_attn_fwd (Kbar/Vbar may be NULL when G == 0), its outputs O and LSE
+ * (LSE required), and dO [B][Hq][n][d].  in_dtype must be bf16
+ * (MSA_ERR_UNSUPPORTED otherwise); O and dO are bf16.  Outputs dQ
+ * [B][Hq][n][d] and dK, dV [B][Hkv][n][d] in out_dtype (bf16 or f32); every
+ * element is written (no accumulation into the caller's buffers).  The
+ * workspace is caller-owned scratch of at least msa_attn_bwd_workspace_size
+ * bytes.  Arithmetic: bf16 matrix-core products with float32 accumulation;
+ * P and dS are rounded to bf16 as operands; each output element is computed
+ * by one workgroup in a fixed order (deterministic, no atomics). */
+msa_status msa_attn_bwd(const msa_attn_desc* desc, const void* Q, const void* K, const void* V,
+                        const void* Kbar, const void* Vbar, const void* O, const float* LSE, const void* dO,
+                        void* workspace, size_t workspace_bytes, void* dQ, void* dK, void* dV,
+                        void* stream);
 
 /* Bytes of device workspace msa_decode_fwd needs:
  * num_splits * batch * heads_q * (head_dim + 1) * 4.  Host only. */

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     decode_partials,
     lib,
     msa_append_kv,
+    msa_attn_bwd,
+    msa_attn_bwd_workspace_size,
     msa_attn_fwd,
     msa_decode_fwd,
     msa_decode_fwd_varlen,
@@ -29,6 +31,7 @@ from .binding import (  # noqa: F401
 
 pool_landmarks = msa_pool_landmarks
 attn_fwd = msa_attn_fwd
+attn_bwd = msa_attn_bwd
 decode_fwd = msa_decode_fwd
 decode_fwd_varlen = msa_decode_fwd_varlen
 append_kv = msa_append_kv

@@ -31,7 +31,7 @@ EXPORTS = (
     "msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
     "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_status_string",
     "msa_last_error", "msa_abi_version", "msa_decode_fwd_varlen", "msa_append_kv",
-    "msa_plan_decode_varlen",
+    "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd",
 )
 
 
@@ -78,9 +78,11 @@ def lib() -> ctypes.CDLL:
         L.msa_decode_fwd_varlen.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.msa_append_kv.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_plan_decode_varlen.argtypes = [P(DecodeDesc), i32, vp, P(i32), P(i32)]
+        L.msa_attn_bwd_workspace_size.argtypes = [P(AttnDesc), P(sz)]
+        L.msa_attn_bwd.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         for f in ("msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
                   "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_decode_fwd_varlen",
-                  "msa_append_kv", "msa_plan_decode_varlen"):
+                  "msa_append_kv", "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -188,6 +190,46 @@ def msa_attn_fwd(Q, K, V, Kbar, Vbar, window: int, num_landmarks: int, scale: Op
     _check(lib().msa_attn_fwd(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
                               _ptr(O), _ptr(LSE), _stream(Q, stream)))
     return O, LSE
+
+
+def msa_attn_bwd_workspace_size(desc: AttnDesc) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().msa_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def msa_attn_bwd(Q, K, V, Kbar, Vbar, O, LSE, dO, window: int, num_landmarks: int,
+                 scale: Optional[float] = None, out_dtype=None, workspace=None, dQ=None, dK=None, dV=None,
+                 stream=None):
+    """Gradients of msa_attn_fwd: (dQ [B][Hq][n][d], dK, dV [B][Hkv][n][d])
+    for the upstream gradient dO, from the forward's O and LSE."""
+    import torch
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, n, d) or V.shape != K.shape or O.shape != Q.shape or dO.shape != Q.shape:
+        raise ValueError("shapes of K, V, O, dO do not match Q")
+    if tuple(LSE.shape) != (B, Hq, n) or LSE.dtype != torch.float32:
+        raise ValueError("LSE must be float32 [B][Hq][n]")
+    if O.dtype != torch.bfloat16 or dO.dtype != torch.bfloat16:
+        raise ValueError("O and dO must be bf16")
+    in_code = _dtype_code(Q.dtype)
+    out_code = MSA_DTYPE_F32 if out_dtype is None else _dtype_code(out_dtype)
+    desc = attn_desc(B, Hq, Hkv, n, d, window, num_landmarks, scale, in_code, out_code)
+    need = msa_attn_bwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    odt = _torch_dtype(out_code)
+    if dQ is None:
+        dQ = torch.empty((B, Hq, n, d), dtype=odt, device=Q.device)
+    if dK is None:
+        dK = torch.empty((B, Hkv, n, d), dtype=odt, device=Q.device)
+    if dV is None:
+        dV = torch.empty((B, Hkv, n, d), dtype=odt, device=Q.device)
+    _check(lib().msa_attn_bwd(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar), _ptr(O),
+                              _ptr(LSE), _ptr(dO), _ptr(workspace), ws_bytes, _ptr(dQ), _ptr(dK), _ptr(dV),
+                              _stream(Q, stream)))
+    return dQ, dK, dV
 
 
 def msa_decode_workspace_size(desc: DecodeDesc) -> int:

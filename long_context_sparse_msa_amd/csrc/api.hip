@@ -167,6 +167,43 @@ msa_status msa_attn_fwd(const msa_attn_desc* desc, const void* Q, const void* K,
   return hip_status(e, "attention launch");
 }
 
+msa_status check_bwd(const msa_attn_desc* d) {
+  msa_status s = check_attn(d);
+  if (s != MSA_OK) return s;
+  if (d->in_dtype != MSA_DTYPE_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "the backward takes bf16 inputs only (in_dtype=%d)", d->in_dtype);
+  const long long rows = (long long)d->batch * d->heads_q * (((long long)d->seq_len + 127) / 128 * 128);
+  if ((rows + 15) / 16 > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MSA_OK;
+}
+
+msa_status msa_attn_bwd_workspace_size(const msa_attn_desc* desc, size_t* bytes) {
+  msa_status s = check_bwd(desc);
+  if (s != MSA_OK) return s;
+  if (bytes == nullptr) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = msa::bwd_layout(*desc).bytes;
+  return ok();
+}
+
+msa_status msa_attn_bwd(const msa_attn_desc* desc, const void* Q, const void* K, const void* V, const void* Kbar,
+                        const void* Vbar, const void* O, const float* LSE, const void* dO, void* workspace,
+                        size_t workspace_bytes, void* dQ, void* dK, void* dV, void* stream) {
+  msa_status s = check_bwd(desc);
+  if (s != MSA_OK) return s;
+  if (desc->batch == 0 || desc->seq_len == 0) return ok();
+  if ((s = check_ptr(Q, "Q")) || (s = check_ptr(K, "K")) || (s = check_ptr(V, "V")) || (s = check_ptr(O, "O")) ||
+      (s = check_ptr(LSE, "LSE")) || (s = check_ptr(dO, "dO")) || (s = check_ptr(workspace, "workspace")) ||
+      (s = check_ptr(dQ, "dQ")) || (s = check_ptr(dK, "dK")) || (s = check_ptr(dV, "dV")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  const size_t need = msa::bwd_layout(*desc).bytes;
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return hip_status(msa::launch_attn_bwd(*desc, Q, K, V, Kbar, Vbar, O, LSE, dO, workspace, dQ, dK, dV,
+                                         static_cast<hipStream_t>(stream)),
+                    "backward launch");
+}
+
 msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes) {
   msa_status s = check_decode(desc);
   if (s != MSA_OK) return s;

@@ -50,32 +50,8 @@ constexpr int BN = kBN_BF16;  // 64
 constexpr int kThreads = 256;
 constexpr float kRescaleTh = 8.0f;  // log2 of the largest unnormalised P
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer: stride 0, num_records in bytes, 32-bit data format
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-
-// (x[l], x[l^32]) for every lane l, as a pair whose max or sum is the
-// value over both halves of the wavefront.
-__device__ __forceinline__ float half_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // ---------------------------------------------------------------------------
 // LDS tiles: 64 rows (keys) x D bf16, row-major, 16-byte chunks permuted

@@ -39,7 +39,6 @@
 namespace msa {
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int kSplitTE = 32;  // entries per tile, split schedule
 constexpr int kFusedTE = 16;  // entries per tile, fused schedule

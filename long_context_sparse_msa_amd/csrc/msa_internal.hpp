@@ -19,6 +19,18 @@ hipError_t launch_attn_f32(const msa_attn_desc& d, const void* Q, const void* K,
                            const void* Kbar, const void* Vbar, void* O, float* LSE,
                            hipStream_t stream);
 
+// Backward workspace layout (bytes) for a prefill problem.
+struct BwdLayout {
+  int n_pad, seg, nseg;
+  size_t ld_off, part_off, lmg_off, bytes;
+};
+BwdLayout bwd_layout(const msa_attn_desc& d);
+
+// Gradients dQ, dK, dV of the bf16 prefill (arguments validated).
+hipError_t launch_attn_bwd(const msa_attn_desc& d, const void* Q, const void* K, const void* V, const void* Kbar,
+                           const void* Vbar, const void* O, const float* LSE, const void* dO, void* workspace,
+                           void* dQ, void* dK, void* dV, hipStream_t stream);
+
 // lens: per-sequence lengths in device memory, or null for ctx_len each.
 hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
                          const void* Kbar, const void* Vbar, const int32_t* lens, float* ws_o, float* ws_lse,

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert sorted(msa.EXPORTS) == names
     for name in names:
         assert hasattr(L, name), name
@@ -265,3 +265,52 @@ def test_plan_decode_varlen_bitexact(C, w, G, S):
         msa.msa_plan_decode_varlen(d, -1)
     # the full length is the static plan
     np.testing.assert_array_equal(msa.msa_plan_decode_varlen(d, C)[0], msa.msa_plan_decode(d)[0])
+
+
+# ---------------------------------------------------------- backward
+
+def call_bwd(desc, ws_bytes=1 << 40, ptr=16, **none):
+    p = ctypes.c_void_p(ptr)
+    args = {k: p for k in ("Q", "K", "V", "Kb", "Vb", "O", "LSE", "dO", "ws", "dQ", "dK", "dV")}
+    for k in none:
+        args[k] = None
+    return msa.lib().msa_attn_bwd(ctypes.byref(desc), args["Q"], args["K"], args["V"], args["Kb"], args["Vb"],
+                                  args["O"], args["LSE"], args["dO"], args["ws"], ws_bytes, args["dQ"],
+                                  args["dK"], args["dV"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), 1), (dict(num_landmarks=3), 1), (dict(heads_q=3), 1), (dict(head_dim=96), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32, out_dtype=msa.MSA_DTYPE_F32), 2), (dict(seq_len=1 << 23), 2),
+    (dict(scale=0.0), 1), (dict(out_dtype=7), 1),
+])
+def test_bwd_validation(kw, status):
+    assert call_bwd(base_desc(**kw)) == status
+
+
+def test_bwd_pointer_and_workspace_checks():
+    d = base_desc()
+    for name in ("Q", "K", "V", "O", "LSE", "dO", "ws", "dQ", "dK", "dV", "Kb", "Vb"):
+        assert call_bwd(d, **{name: 1}) == 1, name
+    assert call_bwd(d, ptr=24) == 1
+    need = msa.msa_attn_bwd_workspace_size(d)
+    assert call_bwd(d, ws_bytes=need - 1) == 3
+    assert call_bwd(base_desc(num_landmarks=0), Kb=1, Vb=1, ws_bytes=msa.msa_attn_bwd_workspace_size(
+        base_desc(num_landmarks=0))) not in (1, 3)  # landmarks not needed without G
+    d0 = base_desc(batch=0)
+    assert call_bwd(d0, ptr=0) == 0
+
+
+def test_bwd_workspace_size_formula():
+    # (lse2, D) per padded row, plus two [B*Hkv][G][2][d] float32 arrays of
+    # landmark gradients (per-segment partials and their sum)
+    for n, G in ((256, 4), (131072, 512), (1000, 0), (1048576, 512)):
+        d = base_desc(seq_len=n, num_landmarks=G, heads_q=64, heads_kv=8)
+        got = msa.msa_attn_bwd_workspace_size(d)
+        n_pad = -(-n // 128) * 128
+        seg = max(4096, -(-n // 32))
+        seg = -(-seg // 32) * 32
+        nseg = -(-n // seg) if G else 0
+        up = lambda x: -(-x // 256) * 256
+        lm = 8 * G * 2 * 128 * 4
+        assert got == up(64 * n_pad * 8) + up(nseg * lm) + up(lm)
