@@ -239,6 +239,43 @@ def incremental_decode(torch, msa, wl, dec, dev, stream, q, Kc, Vc, Kbc, Vbc, ws
             "append_block_bytes": int(B * Hkv * 2 * L * d * 2), "launches": reps}
 
 
+def backward_128k(torch, msa, wl, dev, stream, reps=3):
+    """Secondary line: the backward (msa_attn_bwd: dQ, dK, dV) of the 128K
+    GQA prefill, from the forward's own O and LSE, dO ~ N(0, 1).  FLOPs are
+    counted the usual way for attention backward, 2.5x the forward's: five
+    products per visible pair (S recomputed, dP, dV, dK, dQ), 10*d FLOPs."""
+    cfg = wl.GQA_128K
+    Q, K, V = wl.device_prefill_inputs(cfg, dev)
+    G = cfg.num_landmarks
+    dO = torch.randn(Q.shape, device=dev).to(torch.bfloat16)
+    Kb, Vb = msa.msa_pool_landmarks(K, V, G)
+    O, LSE = msa.msa_attn_fwd(Q, K, V, Kb, Vb, cfg.window, G, cfg.scale)
+    desc = msa.attn_desc(cfg.batch, cfg.heads_q, cfg.heads_kv, cfg.seq_len, cfg.head_dim, cfg.window, G,
+                         cfg.scale, msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_BF16)
+    ws = torch.empty(msa.msa_attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    run = lambda: msa.msa_attn_bwd(Q, K, V, Kb, Vb, O, LSE, dO, cfg.window, G, cfg.scale,
+                                   out_dtype=torch.bfloat16, workspace=ws, dQ=dQ, dK=dK, dV=dV)
+    run()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        run()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / reps
+    win, lm = visible_pairs(cfg.seq_len, cfg.window, G)
+    flops = 10.0 * cfg.head_dim * (win + lm) * cfg.heads_q * cfg.batch
+    del Q, K, V, dO, O, LSE, Kb, Vb, ws, dQ, dK, dV
+    torch.cuda.empty_cache()
+    return {"workload": "gqa_128k backward (n=131072, 64/8 heads, d=128, w=4096, G=512), dQ/dK/dV bf16",
+            "ms": round(ms, 3), "flops_per_launch": flops, "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
+
+
 def measured_peaks(torch, dev, reps=10):
     """Achievable references on this GPU through vendor libraries: a large
     bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
@@ -280,6 +317,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=49152, help="oracle rows per head for the CPU baseline")
     ap.add_argument("--no-1m", action="store_true", help="skip the secondary 1M-token prefill measurement")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured achievable-peak reference runs")
+    ap.add_argument("--no-backward", action="store_true", help="skip the secondary backward measurement")
     ap.add_argument("--no-incremental", action="store_true",
                     help="skip the secondary incremental-decode (append + varlen decode) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -454,6 +492,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_1m:
         out["prefill_1m"] = prefill_1m(torch, msa, wl, dev, stream)
+    if not args.no_backward:
+        out["backward"] = backward_128k(torch, msa, wl, dev, stream)
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
         out["measured_peaks"] = peaks
