@@ -48,6 +48,9 @@ Readings taken where the pages leave the step open:
   landmark's gradient.  The pages train at these lengths but do not write
   the backward out.
 
+* Block-sparse lists: each query block sees the keys of the key blocks
+  listed for it (optionally causal), one softmax; see Step 9.
+
 Every predicate below is evaluated by explicit comparisons; nothing uses a
 closed-form count of visible keys.
 """
@@ -626,3 +629,60 @@ def attn_bwd_dq_rows(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
             pos += len(grp_rows)
         out[h] = (r_all, res)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Step 9: attention over caller-given key blocks (block-sparse lists).  The
+# pages describe block-sparse kernels driven by per-block index lists with
+# counts ("Sparse Attention GPU Cluster Implementation: What Actually Works",
+# section on the kernel that drives the sparse pattern; 64-token blocks) and
+# patterns such as 128-token blocks each attending to 16 others ("Million
+# Token Context Window Optimization: What Actually Works", indexing
+# section).  Reading: query block t (rows t*bq .. t*bq+bq-1) of head h sees
+# every key of the key blocks listed for it (blocks of bk keys, clipped at
+# n), optionally only keys j <= i (causal), under one softmax; a listed
+# block index outside [0, ceil(n/bk)) contributes nothing; a block listed
+# twice is seen twice.  A row that sees nothing has O = 0, LSE = -inf.
+# ---------------------------------------------------------------------------
+
+def blocksparse_mask(n: int, counts, indices, bq: int, bk: int, causal: bool) -> np.ndarray:
+    """Multiplicity of each (row, key) pair for one head: int [n, n]."""
+    nkb = -(-n // bk)
+    M = np.zeros((n, n), dtype=np.int64)
+    for t in range(-(-n // bq)):
+        r0, r1 = t * bq, min(n, (t + 1) * bq)
+        for c in range(int(counts[t])):
+            kb = int(indices[t][c])
+            if kb < 0 or kb >= nkb:
+                continue
+            M[r0:r1, kb * bk:min(n, (kb + 1) * bk)] += 1
+    if causal:
+        M = np.tril(M)
+    return M
+
+
+def attn_blocksparse(Q, K, V, counts, indices, bq: int, bk: int, causal: bool, scale: Optional[float] = None):
+    """O [B, Hq, n, d], LSE [B, Hq, n] for per-(batch, query head) block
+    lists: counts [B, Hq, T], indices [B, Hq, T, max_blocks]."""
+    Q = np.asarray(Q, dtype=np.float64)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, n, d))
+    LSE = np.full((B, Hq, n), NEG_INF)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            M = blocksparse_mask(n, counts[b][h], indices[b][h], bq, bk, causal)
+            k = np.asarray(K[b, g], np.float64)
+            v = np.asarray(V[b, g], np.float64)
+            S = scale * (Q[b, h] @ k.T)
+            vis = M > 0
+            m = np.where(vis, S, NEG_INF).max(axis=1)
+            live = np.isfinite(m)
+            E = np.where(vis, M * np.exp(S - np.where(live, m, 0.0)[:, None]), 0.0)
+            l = E.sum(axis=1)
+            O[b, h, live] = (E[live] @ v) / l[live, None]
+            LSE[b, h, live] = m[live] + np.log(l[live])
+    return O, LSE

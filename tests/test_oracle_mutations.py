@@ -5,6 +5,7 @@ import pytest
 
 from oracle import msa_oracle as orc
 from tests import test_oracle_backward as bwd
+from tests import test_oracle_blocksparse as bsp
 from tests import test_oracle_incremental as inc
 from tests import test_oracle_pins as pins
 
@@ -92,6 +93,17 @@ def _mean_bwd_last_row(dXbar, L):               # sends the whole gradient to th
     return out
 
 
+def _bs_mask_strict_causal(n, counts, indices, bq, bk, causal):   # causal without the diagonal
+    M = orc.__dict__["_orig_bs_mask"](n, counts, indices, bq, bk, False)
+    return np.tril(M, -1) if causal else M
+
+
+def _bs_mask_block_short(n, counts, indices, bq, bk, causal):      # drops each block's last key
+    M = orc.__dict__["_orig_bs_mask"](n, counts, indices, bq, bk, causal)
+    M[:, bk - 1::bk] = 0
+    return M
+
+
 MUTANTS = {
     "window_wide": ("window_visible", _window_wide),
     "window_no_self": ("window_visible", _window_no_self),
@@ -108,6 +120,8 @@ MUTANTS = {
     "bwd_no_rowsum": ("_softmax_bwd", _softmax_bwd_no_rowsum),
     "bwd_mean_no_divide": ("_mean_bwd", _mean_bwd_no_divide),
     "bwd_mean_last_row": ("_mean_bwd", _mean_bwd_last_row),
+    "bs_strict_causal": ("blocksparse_mask", _bs_mask_strict_causal),
+    "bs_block_short": ("blocksparse_mask", _bs_mask_block_short),
 }
 
 PIN_SET = [
@@ -128,6 +142,8 @@ PIN_SET = [
     lambda: inc.test_append_then_decode_equals_decode_of_the_whole_prefix(),
     lambda: bwd.test_backward_matches_finite_differences(9, 4, 3),
     lambda: bwd.test_one_token_landmarks_give_causal_backward(7),
+    lambda: bsp.test_full_causal_lists_are_causal_sdpa(),
+    lambda: bsp.test_brute_force_random_lists(True),
 ]
 
 
@@ -153,5 +169,6 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(orc.__dict__, "_orig_merge", orc.merge)
     monkeypatch.setitem(orc.__dict__, "_orig_vlf", orc.visible_list_fixed)
     monkeypatch.setitem(orc.__dict__, "_orig_pool_prefix", orc.pool_prefix)
+    monkeypatch.setitem(orc.__dict__, "_orig_bs_mask", orc.blocksparse_mask)
     monkeypatch.setattr(orc, attr, fn)
     assert _failures() > 0, f"no pin caught the planted mistake {name}"
