@@ -276,6 +276,40 @@ def backward_128k(torch, msa, wl, dev, stream, reps=3):
             "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
 
 
+def blocksparse_band_128k(torch, msa, wl, dev, stream, reps=3):
+    """Secondary line: msa_attn_fwd_blocksparse on the 128K GQA shapes with
+    the band pattern of 128-token blocks each attending to the 16 blocks
+    around it (non-causal).  FLOPs: 4*d per (row, listed key) pair."""
+    cfg = wl.GQA_128K
+    Q, K, V = wl.device_prefill_inputs(cfg, dev)
+    counts, idx = wl.band_block_lists(cfg.batch, cfg.heads_q, cfg.seq_len)
+    cd, id_ = torch.from_numpy(counts).to(dev), torch.from_numpy(idx).to(dev)
+    O = torch.empty_like(Q)
+    LSE = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    run = lambda: msa.msa_attn_fwd_blocksparse(Q, K, V, cd, id_, False, cfg.scale, O=O, LSE=LSE)
+    run()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        run()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / reps
+    n = cfg.seq_len
+    keys_per_tile = [sum(min(n, (kb + 1) * 64) - kb * 64 for kb in idx[0, 0, t, :counts[0, 0, t]])
+                     for t in range(counts.shape[2])]
+    rows_per_tile = [min(n, (t + 1) * 128) - t * 128 for t in range(counts.shape[2])]
+    pairs = sum(k * r for k, r in zip(keys_per_tile, rows_per_tile))
+    flops = 4.0 * cfg.head_dim * pairs * cfg.heads_q * cfg.batch
+    del Q, K, V, O, LSE, cd, id_
+    torch.cuda.empty_cache()
+    return {"workload": "gqa_128k shapes, block-sparse lists: each 128-token block attends to the 16 blocks "
+                        "around it (non-causal)", "ms": round(ms, 3), "flops_per_launch": flops,
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
+
+
 def measured_peaks(torch, dev, reps=10):
     """Achievable references on this GPU through vendor libraries: a large
     bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
@@ -318,6 +352,8 @@ def main():
     ap.add_argument("--no-1m", action="store_true", help="skip the secondary 1M-token prefill measurement")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured achievable-peak reference runs")
     ap.add_argument("--no-backward", action="store_true", help="skip the secondary backward measurement")
+    ap.add_argument("--no-blocksparse", action="store_true",
+                    help="skip the secondary block-sparse-list measurement")
     ap.add_argument("--no-incremental", action="store_true",
                     help="skip the secondary incremental-decode (append + varlen decode) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -494,6 +530,8 @@ def main():
         out["prefill_1m"] = prefill_1m(torch, msa, wl, dev, stream)
     if not args.no_backward:
         out["backward"] = backward_128k(torch, msa, wl, dev, stream)
+    if not args.no_blocksparse:
+        out["blocksparse"] = blocksparse_band_128k(torch, msa, wl, dev, stream)
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
         out["measured_peaks"] = peaks

@@ -54,8 +54,9 @@ extern "C" {
 #endif
 
 /* 1: pooling, prefill, static decode and plans.  2: adds incremental
- * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen) and
- * the backward (msa_attn_bwd_workspace_size, msa_attn_bwd). */
+ * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen),
+ * the backward (msa_attn_bwd_workspace_size, msa_attn_bwd) and block-sparse
+ * lists (msa_attn_fwd_blocksparse). */
 #define MSA_ABI_VERSION 2
 
 typedef enum {
@@ -126,6 +127,36 @@ msa_status msa_pool_landmarks(const msa_attn_desc* desc, const void* K, const vo
  * Attention paragraph of "Training at 1M+ Token Context ...". */
 msa_status msa_attn_fwd(const msa_attn_desc* desc, const void* Q, const void* K, const void* V,
                         const void* Kbar, const void* Vbar, void* O, float* LSE, void* stream);
+
+/* ---- Block-sparse lists: the same tiled pass driven by explicit per-block
+ * lists instead of the window + landmark closed form.  The pages drive
+ * block-sparse kernels by per-block index lists with counts ("Sparse
+ * Attention GPU Cluster Implementation: What Actually Works", section on
+ * the kernel that applies the pattern; 64-token blocks) and describe
+ * patterns such as 128-token blocks each attending to 16 others ("Million
+ * Token Context Window Optimization: What Actually Works", indexing
+ * section). ---- */
+
+#define MSA_LIST_QUERY_BLOCK 128 /* rows per query block of a list     */
+#define MSA_LIST_KEY_BLOCK 64    /* keys per listed key block           */
+
+/* O and LSE where query block t (rows t*128 .. t*128+127) of query head h
+ * in batch b sees every key of the key blocks listed for it -- block k
+ * covers keys k*64 .. k*64+63, clipped at n -- and, with causal = 1, only
+ * keys j <= i; one softmax over what a row sees.  Lists live in device
+ * memory: block_counts int32 [B][Hq][T] (T = ceil(n/128)), block_indices
+ * int32 [B][Hq][T][max_blocks]; entry c < count of a list is its c-th
+ * block (order free).  Counts are clamped to [0, max_blocks] on the
+ * device; an index outside [0, ceil(n/64)) is skipped; a block listed
+ * twice is seen twice.  A row that sees nothing gets O = 0, LSE = -inf.
+ * desc fields read: batch, heads_q, heads_kv, seq_len, head_dim, scale,
+ * in_dtype (bf16 only, MSA_ERR_UNSUPPORTED otherwise), out_dtype; window
+ * and num_landmarks are not read.  LSE may be NULL.  Other conventions as
+ * for msa_attn_fwd. */
+msa_status msa_attn_fwd_blocksparse(const msa_attn_desc* desc, const int32_t* block_counts,
+                                   const int32_t* block_indices, int32_t max_blocks, int32_t causal,
+                                   const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                   void* stream);
 
 /* ---- Backward of msa_attn_fwd.  The pages train at these lengths
  * ("Training at 1M+ Token Context: Ring Attention, YaRN, NTK-Aware Scaling

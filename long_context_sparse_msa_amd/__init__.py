@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     msa_attn_bwd,
     msa_attn_bwd_workspace_size,
     msa_attn_fwd,
+    msa_attn_fwd_blocksparse,
     msa_decode_fwd,
     msa_decode_fwd_varlen,
     msa_decode_workspace_size,
@@ -32,6 +33,7 @@ from .binding import (  # noqa: F401
 pool_landmarks = msa_pool_landmarks
 attn_fwd = msa_attn_fwd
 attn_bwd = msa_attn_bwd
+attn_fwd_blocksparse = msa_attn_fwd_blocksparse
 decode_fwd = msa_decode_fwd
 decode_fwd_varlen = msa_decode_fwd_varlen
 append_kv = msa_append_kv

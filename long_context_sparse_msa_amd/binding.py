@@ -31,8 +31,11 @@ EXPORTS = (
     "msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
     "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_status_string",
     "msa_last_error", "msa_abi_version", "msa_decode_fwd_varlen", "msa_append_kv",
-    "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd",
+    "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd", "msa_attn_fwd_blocksparse",
 )
+
+LIST_QUERY_BLOCK = 128
+LIST_KEY_BLOCK = 64
 
 
 class MsaError(RuntimeError):
@@ -79,10 +82,12 @@ def lib() -> ctypes.CDLL:
         L.msa_append_kv.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_plan_decode_varlen.argtypes = [P(DecodeDesc), i32, vp, P(i32), P(i32)]
         L.msa_attn_bwd_workspace_size.argtypes = [P(AttnDesc), P(sz)]
+        L.msa_attn_fwd_blocksparse.argtypes = [P(AttnDesc), vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
         L.msa_attn_bwd.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         for f in ("msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
                   "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_decode_fwd_varlen",
-                  "msa_append_kv", "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd"):
+                  "msa_append_kv", "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd",
+                  "msa_attn_fwd_blocksparse"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -189,6 +194,35 @@ def msa_attn_fwd(Q, K, V, Kbar, Vbar, window: int, num_landmarks: int, scale: Op
     desc = attn_desc(B, Hq, Hkv, n, d, window, num_landmarks, scale, in_code, out_code)
     _check(lib().msa_attn_fwd(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
                               _ptr(O), _ptr(LSE), _stream(Q, stream)))
+    return O, LSE
+
+
+def msa_attn_fwd_blocksparse(Q, K, V, block_counts, block_indices, causal: bool, scale: Optional[float] = None,
+                             out_dtype=None, O=None, LSE=None, want_lse: bool = True, stream=None):
+    """Attention over listed 64-key blocks per 128-row query block:
+    block_counts int32 [B][Hq][T], block_indices int32 [B][Hq][T][max_blocks]
+    (device tensors).  Returns (O, LSE)."""
+    import torch
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    T = -(-n // LIST_QUERY_BLOCK)
+    if K.shape != (B, Hkv, n, d) or V.shape != K.shape:
+        raise ValueError("K/V shapes do not match Q")
+    if block_counts.dtype != torch.int32 or tuple(block_counts.shape) != (B, Hq, T):
+        raise ValueError(f"block_counts must be int32 [{B}][{Hq}][{T}]")
+    if block_indices.dtype != torch.int32 or block_indices.dim() != 4 or \
+            tuple(block_indices.shape[:3]) != (B, Hq, T):
+        raise ValueError(f"block_indices must be int32 [{B}][{Hq}][{T}][max_blocks]")
+    in_code = _dtype_code(Q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    if O is None:
+        O = torch.empty((B, Hq, n, d), dtype=_torch_dtype(out_code), device=Q.device)
+    if LSE is None and want_lse:
+        LSE = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device)
+    desc = attn_desc(B, Hq, Hkv, n, d, 1, 0, scale, in_code, out_code)
+    _check(lib().msa_attn_fwd_blocksparse(ctypes.byref(desc), _ptr(block_counts), _ptr(block_indices),
+                                          int(block_indices.shape[3]), 1 if causal else 0, _ptr(Q), _ptr(K),
+                                          _ptr(V), _ptr(O), _ptr(LSE), _stream(Q, stream)))
     return O, LSE
 
 

@@ -167,6 +167,32 @@ msa_status msa_attn_fwd(const msa_attn_desc* desc, const void* Q, const void* K,
   return hip_status(e, "attention launch");
 }
 
+msa_status msa_attn_fwd_blocksparse(const msa_attn_desc* desc, const int32_t* block_counts,
+                                   const int32_t* block_indices, int32_t max_blocks, int32_t causal, const void* Q,
+                                   const void* K, const void* V, void* O, float* LSE, void* stream) {
+  if (desc == nullptr) return fail(MSA_ERR_INVALID_ARG, "desc is NULL");
+  msa_attn_desc d = *desc;
+  d.window = 1;         // not read by this entry point
+  d.num_landmarks = 0;  // not read by this entry point
+  msa_status s = check_attn(&d);
+  if (s != MSA_OK) return s;
+  if (d.in_dtype != MSA_DTYPE_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "block-sparse lists take bf16 inputs only (in_dtype=%d)", d.in_dtype);
+  if (max_blocks < 0) return fail(MSA_ERR_INVALID_ARG, "max_blocks=%d < 0", max_blocks);
+  if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+  if (d.batch == 0 || d.seq_len == 0) return ok();
+  if ((s = check_ptr(Q, "Q")) || (s = check_ptr(K, "K")) || (s = check_ptr(V, "V")) || (s = check_ptr(O, "O")))
+    return s;
+  if (block_counts == nullptr || (reinterpret_cast<uintptr_t>(block_counts) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "block_counts is NULL or not 4-byte aligned");
+  if (max_blocks > 0 && (block_indices == nullptr || (reinterpret_cast<uintptr_t>(block_indices) & 3u) != 0))
+    return fail(MSA_ERR_INVALID_ARG, "block_indices is NULL or not 4-byte aligned");
+  if (LSE != nullptr && !aligned16(LSE)) return fail(MSA_ERR_INVALID_ARG, "LSE is not 16-byte aligned");
+  return hip_status(msa::launch_attn_list_bf16(d, block_counts, block_indices, max_blocks, causal, Q, K, V, O, LSE,
+                                               static_cast<hipStream_t>(stream)),
+                    "block-sparse attention launch");
+}
+
 msa_status check_bwd(const msa_attn_desc* d) {
   msa_status s = check_attn(d);
   if (s != MSA_OK) return s;

@@ -475,6 +475,157 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
 }
 
+// ---------------------------------------------------------------------------
+// Block-sparse lists: query tile t of head h visits the 64-key blocks listed
+// for it (block index kb covers keys kb*64 .. kb*64+63, clipped at n),
+// optionally causal, with the same tile pipeline as the window walk.  An
+// index outside [0, ceil(n/64)) loads nothing and is skipped.
+template <int D>
+struct ListWalk {
+  const int32_t* idx;
+  int count, nkb, n;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  // First key of list entry it; n (no tile) past the end or out of range.
+  __device__ int key0(int it) const {
+    if (it >= count) return n;
+    const int kb = idx[it];
+    return (kb >= 0 && kb < nkb) ? kb * BN : n;
+  }
+};
+
+// -inf on every score of tile key0 that this lane's row does not see.
+__device__ __forceinline__ void mask_list_tile(f32x16* s, int key0, int row, int n, bool causal, int g2) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + mb * 32 + jj * 8 + g2 * 4 + i;
+        const bool vis = key < n && (!causal || key <= row);
+        s[mb][jj * 4 + i] = vis ? s[mb][jj * 4 + i] : -INFINITY;
+      }
+    }
+  }
+}
+
+template <int D, int BUF>
+__device__ __forceinline__ void list_tile_step(int key_cur, int key_nxt, bool causal, unsigned char* smem,
+                                               const Stager<D>& sg, const ListWalk<D>& wk, const Frag<D>& fr,
+                                               const bf16x8* qf, RowState<D>& st, const TileCtx& tc) {
+  using SM = Smem<D>;
+  sg.issue_k(wk.rk, smem + SM::kbuf(BUF ^ 1), key_nxt);
+  sg.issue_v(wk.rv, smem + SM::vbuf(BUF ^ 1), key_nxt);
+  const bool any = key_cur < wk.n && (!causal || key_cur <= tc.wr1);
+  const bool interior = key_cur + BN <= wk.n && (!causal || key_cur + BN - 1 <= tc.wr0);
+  if (tc.live && any) {
+    f32x16 s[2];
+    bf16x8 pf[4];
+    mma_phase<D, false, true>(nullptr, smem + SM::kbuf(BUF), fr, qf, pf, st.o, s);
+    if (!interior) mask_list_tile(s, key_cur, tc.row, wk.n, causal, tc.g2);
+    softmax_tile<D>(s, tc.c2, st, pf);
+    mma_phase<D, true, false>(smem + SM::vbuf(BUF), nullptr, fr, qf, pf, st.o, s);
+  }
+  lds_loads_done_barrier();
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_list_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ indices, int max_blocks, int causal_i,
+    void* __restrict__ Out, float* __restrict__ LSE, int Hq, int Hkv, int n, float c2, int T) {
+  using SM = Smem<D>;
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+
+  const int j = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = Hq / Hkv;
+  const int h_in = j % grp;
+  int rest = j / grp;
+  const int t = rest % T;
+  rest /= T;
+  const int kvh = rest % Hkv;
+  const int b = rest / Hkv;
+  const int h = kvh * grp + h_in;
+  const bool causal = causal_i != 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int g2 = lane >> 5;
+
+  zero_smem<D>(smem, tid, kThreads);
+
+  ListWalk<D> wk;
+  const size_t list = ((size_t)b * Hq + h) * T + t;
+  const int cnt = counts[list];
+  wk.count = cnt < 0 ? 0 : (cnt > max_blocks ? max_blocks : cnt);
+  wk.idx = indices + list * (size_t)max_blocks;
+  wk.nkb = (n + BN - 1) / BN;
+  wk.n = n;
+  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)n * D;
+  wk.rk = make_rsrc(K + kv_off, (uint32_t)n * D * 2u);
+  wk.rv = make_rsrc(V + kv_off, (uint32_t)n * D * 2u);
+
+  const int wr0 = t * BM + wave * 32;
+  const int wr1 = min(wr0 + 31, n - 1);
+  const int row = wr0 + r32;
+  const bool live = wr0 <= n - 1;
+
+  const size_t q_off = ((size_t)b * Hq + h) * (size_t)n * D;
+  bf16x8 qf[D / 16];
+  load_q<D>(Q, q_off, row, n, g2, qf);
+
+  RowState<D> st;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
+  st.m = -1e30f;
+  st.l = 0.f;
+  st.ls = 0.f;
+
+  Stager<D> sg;
+  sg.init(tid);
+  Frag<D> fr;
+  fr.init(lane);
+  __syncthreads();  // zeroed buffers in place before any load lands
+
+  int key_cur = wk.key0(0);
+  int key_nxt = wk.key0(1);
+  sg.issue_k(wk.rk, smem + SM::kbuf(0), key_cur);
+  sg.issue_v(wk.rv, smem + SM::vbuf(0), key_cur);
+  lds_loads_done_barrier();
+
+  // the list entry two ahead is read while the current tile computes
+  const TileCtx tc{wr0, wr1, 0, 0, 0, row, 0, g2, live, c2};
+  int it = 0;
+  for (; it + 1 < wk.count; it += 2) {
+    int key_2 = wk.key0(it + 2);
+    list_tile_step<D, 0>(key_cur, key_nxt, causal, smem, sg, wk, fr, qf, st, tc);
+    key_cur = key_nxt;
+    key_nxt = key_2;
+    key_2 = wk.key0(it + 3);
+    list_tile_step<D, 1>(key_cur, key_nxt, causal, smem, sg, wk, fr, qf, st, tc);
+    key_cur = key_nxt;
+    key_nxt = key_2;
+  }
+  if (it < wk.count) list_tile_step<D, 0>(key_cur, key_nxt, causal, smem, sg, wk, fr, qf, st, tc);
+  store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_list_t(const msa_attn_desc& d, const int32_t* counts, const int32_t* indices, int max_blocks,
+                         int causal, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                         hipStream_t stream) {
+  const int n = d.seq_len;
+  const int T = (n + BM - 1) / BM;
+  const long long wgs = (long long)d.batch * d.heads_q * T;
+  hipLaunchKernelGGL((attn_fwd_list_kernel<D, OUT_BF16>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), counts, indices, max_blocks, causal, O, LSE, d.heads_q,
+                     d.heads_kv, n, d.scale * kLog2e, T);
+  return hipGetLastError();
+}
+
 template <int D, bool OUT_BF16>
 hipError_t launch_t(const msa_attn_desc& d, const void* Q, const void* K, const void* V,
                     const void* Kb, const void* Vb, void* O, float* LSE, hipStream_t stream) {
@@ -494,6 +645,18 @@ hipError_t launch_t(const msa_attn_desc& d, const void* Q, const void* K, const 
 }
 
 }  // namespace
+
+hipError_t launch_attn_list_bf16(const msa_attn_desc& d, const int32_t* counts, const int32_t* indices,
+                                 int max_blocks, int causal, const void* Q, const void* K, const void* V, void* O,
+                                 float* LSE, hipStream_t stream) {
+  const bool ob = d.out_dtype == MSA_DTYPE_BF16;
+  if (d.head_dim == 128) {
+    return ob ? launch_list_t<128, true>(d, counts, indices, max_blocks, causal, Q, K, V, O, LSE, stream)
+              : launch_list_t<128, false>(d, counts, indices, max_blocks, causal, Q, K, V, O, LSE, stream);
+  }
+  return ob ? launch_list_t<64, true>(d, counts, indices, max_blocks, causal, Q, K, V, O, LSE, stream)
+            : launch_list_t<64, false>(d, counts, indices, max_blocks, causal, Q, K, V, O, LSE, stream);
+}
 
 hipError_t launch_attn_bf16(const msa_attn_desc& d, const void* Q, const void* K, const void* V,
                             const void* Kbar, const void* Vbar, void* O, float* LSE,

@@ -15,6 +15,12 @@ hipError_t launch_attn_bf16(const msa_attn_desc& d, const void* Q, const void* K
                             const void* Kbar, const void* Vbar, void* O, float* LSE,
                             hipStream_t stream);
 
+// Attention over per-(batch, query head, 128-row query tile) lists of
+// 64-key blocks (arguments validated; lists in device memory).
+hipError_t launch_attn_list_bf16(const msa_attn_desc& d, const int32_t* counts, const int32_t* indices,
+                                 int max_blocks, int causal, const void* Q, const void* K, const void* V, void* O,
+                                 float* LSE, hipStream_t stream);
+
 hipError_t launch_attn_f32(const msa_attn_desc& d, const void* Q, const void* K, const void* V,
                            const void* Kbar, const void* Vbar, void* O, float* LSE,
                            hipStream_t stream);

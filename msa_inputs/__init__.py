@@ -177,6 +177,42 @@ def decode_lengths(batch: int, capacity: int, seed: int = SEED_PLAIN, lo_frac: f
     return rng.integers(lo, capacity + 1, size=batch).astype(np.int32)
 
 
+def band_block_lists(batch: int, heads: int, n: int, blocks: int = 16, block_tokens: int = 128,
+                     query_block: int = 128, key_block: int = 64):
+    """Block lists of the pattern in which each 128-token block attends to 16
+    blocks around it, half to the left and half to the right ("Million Token
+    Context Window Optimization: What Actually Works", indexing section):
+    query block t lists the 128-token blocks t - blocks/2 .. t + blocks/2 - 1
+    (clipped to the sequence), written as key_block-sized indices.  Returns
+    (counts int32 [B][H][T], indices int32 [B][H][T][max_blocks])."""
+    T = -(-n // query_block)
+    per = block_tokens // key_block
+    nkb = -(-n // key_block)
+    maxb = blocks * per
+    counts = np.zeros((batch, heads, T), np.int32)
+    idx = np.full((batch, heads, T, maxb), -1, np.int32)
+    for t in range(T):
+        c0 = t * query_block // block_tokens
+        kbs = [kb for c in range(c0 - blocks // 2, c0 + blocks // 2) if c >= 0
+               for kb in range(c * per, (c + 1) * per) if kb < nkb]
+        counts[:, :, t] = len(kbs)
+        idx[:, :, t, :len(kbs)] = kbs
+    return counts, idx
+
+
+def random_block_lists(batch: int, heads: int, n: int, max_blocks: int, seed: int,
+                       query_block: int = 128, key_block: int = 64):
+    """Seeded random lists for tests: counts uniform in [0, max_blocks],
+    indices uniform in [-2, nkb + 2) (so some are out of range), repeats
+    allowed."""
+    rng = np.random.default_rng(2000 + seed)
+    T = -(-n // query_block)
+    nkb = -(-n // key_block)
+    counts = rng.integers(0, max_blocks + 1, size=(batch, heads, T)).astype(np.int32)
+    idx = rng.integers(-2, nkb + 2, size=(batch, heads, T, max_blocks)).astype(np.int32)
+    return counts, idx
+
+
 def sample_rows(n: int, head: int, count: int = 4096, window: int = 0, block: int = 0) -> np.ndarray:
     """Seeded sample of query rows for one head (generator seeded 12345+head),
     plus forced edge rows around the start, the window edge, the first

@@ -686,3 +686,39 @@ def attn_blocksparse(Q, K, V, counts, indices, bq: int, bk: int, causal: bool, s
             O[b, h, live] = (E[live] @ v) / l[live, None]
             LSE[b, h, live] = m[live] + np.log(l[live])
     return O, LSE
+
+
+def attn_blocksparse_rows(Q, K, V, counts, indices, bq: int, bk: int, causal: bool, scale: Optional[float] = None,
+                          rows: Optional[Dict[int, np.ndarray]] = None):
+    """Selected rows of attn_blocksparse: {head: (rows, O [B, R, d],
+    LSE [B, R])}.  Each row's keys are gathered from its query block's list
+    (with multiplicity) and the causal predicate applied to each."""
+    Q = np.asarray(Q)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nkb = -(-n // bk)
+    out = {}
+    for h in sorted(rows):
+        g = kv_head(h, Hq, Hkv)
+        r_all = np.asarray(rows[h], dtype=np.int64)
+        O = np.zeros((B, len(r_all), d))
+        LSE = np.full((B, len(r_all)), NEG_INF)
+        for b in range(B):
+            for k, i in enumerate(r_all):
+                t = int(i) // bq
+                keys = [j for c in range(int(counts[b][h][t]))
+                        for kb in [int(indices[b][h][t][c])] if 0 <= kb < nkb
+                        for j in range(kb * bk, min(n, (kb + 1) * bk))]
+                keys = np.array([j for j in keys if not causal or j <= i], dtype=np.int64)
+                if len(keys) == 0:
+                    continue
+                q = np.asarray(Q[b, h, i], np.float64)
+                sc = scale * (np.asarray(K[b, g, keys], np.float64) @ q)
+                m = sc.max()
+                p = np.exp(sc - m)
+                O[b, k] = (p @ np.asarray(V[b, g, keys], np.float64)) / p.sum()
+                LSE[b, k] = m + np.log(p.sum())
+        out[h] = (r_all, O, LSE)
+    return out

@@ -120,3 +120,17 @@ def test_rows_that_see_nothing():
     O, L = orc.attn_blocksparse(Q, K, V, counts, idx, bs, bs, True, SC)
     assert (O[0, 0, :16] == 0).all() and np.isneginf(L[0, 0, :16]).all()
     assert np.isfinite(L[0, 0, 16:]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_version_equals_dense(causal):
+    n, bq, bk = 200, 32, 16
+    Q, K, V = rnd((2, 4, n, 8), 20), rnd((2, 2, n, 8), 21), rnd((2, 2, n, 8), 22)
+    rng = np.random.default_rng(23)
+    T, nkb = -(-n // bq), -(-n // bk)
+    counts, idx = lists_from(lambda b, h, t: list(rng.integers(-2, nkb + 2, size=rng.integers(0, 9))), 2, 4, T, 8)
+    O, L = orc.attn_blocksparse(Q, K, V, counts, idx, bq, bk, causal, SC)
+    rows = {h: np.sort(np.random.default_rng(h).choice(n, 30, replace=False)) for h in (0, 3)}
+    for h, (r, o, l) in orc.attn_blocksparse_rows(Q, K, V, counts, idx, bq, bk, causal, SC, rows).items():
+        np.testing.assert_allclose(o, O[:, h, r], atol=1e-12)
+        np.testing.assert_allclose(l, L[:, h, r], atol=1e-12)
