@@ -310,6 +310,62 @@ def blocksparse_band_128k(torch, msa, wl, dev, stream, reps=3):
             "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
 
 
+def paged_decode(torch, msa, wl, dev, stream, page=64, reps=5):
+    """Secondary line: the incremental-decode step on paged caches -- pools of
+    64-row pages, each sequence's pages scattered by a seeded permutation --
+    at the decode workload's shapes and the same seeded lengths: append one
+    token per sequence, then decode (last-level cache flushed by a read
+    before each decode)."""
+    dec = wl.DECODE_512K
+    B, Hq, Hkv, C, d, G = dec.batch, dec.heads_q, dec.heads_kv, dec.ctx_len, dec.head_dim, dec.num_landmarks
+    P = C // page
+    n_pages = B * P
+    Kp = torch.empty((n_pages, Hkv, page, d), dtype=torch.bfloat16, device=dev).normal_()
+    Vp = torch.empty_like(Kp).normal_()
+    perm = torch.from_numpy(__import__("numpy").random.default_rng(7).permutation(n_pages).reshape(B, P)
+                            .astype("int32")).to(dev)
+    Kb = torch.randn((B, Hkv, G, d), device=dev).to(torch.bfloat16)
+    Vb = torch.randn((B, Hkv, G, d), device=dev).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), device=dev).to(torch.bfloat16)
+    lens = wl.decode_lengths(B, C - 1)
+    pos_d = torch.from_numpy(lens).to(dev)
+    lens_d = pos_d + 1
+    k_new = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+    v_new = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+    ddesc = msa.decode_desc(B, Hq, Hkv, C, d, dec.window, G, dec.num_splits)
+    ws = torch.empty(msa.msa_decode_workspace_size(ddesc) // 4, dtype=torch.float32, device=dev)
+    O = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def once(ev):
+        torch.sum(flush, dim=(0,), dtype=torch.float32, out=sink)
+        ev[0].record(stream)
+        msa.msa_append_kv_paged(k_new, v_new, pos_d, Kp, Vp, perm, Kb, Vb, G)
+        ev[1].record(stream)
+        msa.msa_decode_fwd_paged(q, Kp, Vp, perm, Kb, Vb, lens_d, dec.window, G, dec.num_splits, dec.scale,
+                                 workspace=ws, O=O, LSE=LSE)
+        ev[2].record(stream)
+
+    once([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for ev in evs:
+        once(ev)
+    torch.cuda.synchronize()
+    app = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+    dms = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
+    entries = sum(msa.msa_plan_decode_varlen(ddesc, int(n) + 1)[2] for n in lens)
+    nbytes = Hkv * entries * d * 2 * 2 + B * Hq * (d * 2 * 2 + 4)
+    gbs = nbytes / (dms * 1e-3) / 1e9
+    del Kp, Vp, perm, Kb, Vb, q, ws, O, LSE, flush, sink
+    torch.cuda.empty_cache()
+    return {"workload": f"paged caches ({page}-row pages, pages of each sequence scattered by a seeded "
+                        f"permutation), {B} sequences, capacity {C}, same lengths as incremental_decode",
+            "decode_ms": round(dms, 4), "decode_GBps": round(gbs, 1), "decode_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": nbytes, "append_ms": round(app, 4), "launches": reps}
+
+
 def measured_peaks(torch, dev, reps=10):
     """Achievable references on this GPU through vendor libraries: a large
     bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
@@ -526,6 +582,8 @@ def main():
                                                        Od, Ld, flush, flush_sink)
     del q, Kc, Vc, ws, flush, flush_sink
     torch.cuda.empty_cache()
+    if not args.no_incremental:
+        out["paged_decode"] = paged_decode(torch, msa, wl, dev, stream)
     if not args.no_1m:
         out["prefill_1m"] = prefill_1m(torch, msa, wl, dev, stream)
     if not args.no_backward:

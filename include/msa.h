@@ -54,7 +54,8 @@ extern "C" {
 #endif
 
 /* 1: pooling, prefill, static decode and plans.  2: adds incremental
- * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen),
+ * decode (msa_decode_fwd_varlen, msa_append_kv, msa_plan_decode_varlen, and
+ * the paged msa_decode_fwd_paged, msa_append_kv_paged),
  * the backward (msa_attn_bwd_workspace_size, msa_attn_bwd) and block-sparse
  * lists (msa_attn_fwd_blocksparse). */
 #define MSA_ABI_VERSION 2
@@ -189,8 +190,9 @@ msa_status msa_attn_bwd(const msa_attn_desc* desc, const void* Q, const void* K,
                         void* workspace, size_t workspace_bytes, void* dQ, void* dK, void* dV,
                         void* stream);
 
-/* Bytes of device workspace msa_decode_fwd needs:
- * num_splits * batch * heads_q * (head_dim + 1) * 4.  Host only. */
+/* Bytes of device workspace msa_decode_fwd (and its _varlen and _paged
+ * forms) needs: num_splits * batch * heads_q * (head_dim + 1) * 4.  Host
+ * only; the 2 GiB limit of contiguous caches is not checked here. */
 msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes);
 
 /* Decode with split-KV partial softmax and an LSE merge.
@@ -262,6 +264,30 @@ msa_status msa_decode_fwd_varlen(const msa_decode_desc* desc, const int32_t* ctx
 msa_status msa_append_kv(const msa_decode_desc* desc, const int32_t* positions, const void* k_new,
                          const void* v_new, void* Kcache, void* Vcache, void* Kbar, void* Vbar,
                          void* stream);
+
+/* Paged caches (the vLLM-style "PagedAttention" the page "Sparse Attention
+ * GPU Cluster Implementation: What Actually Works", FAQ, names for
+ * single-node serving): K and V rows live in pools of fixed-size pages,
+ * Kpages, Vpages [num_pages][Hkv][page_size][d] bf16, and sequence b's
+ * logical page p (rows p*page_size .. +page_size-1) is physical page
+ * block_table[b][p] (int32 device array [B][C/page_size], C =
+ * desc->ctx_len, the capacity).  page_size is a power of two in [32, 2^20]
+ * dividing C.  Landmarks stay contiguous, [B][Hkv][G][d].  A page id
+ * outside [0, num_pages) is never dereferenced: decode reads page 0 in its
+ * place (the result for that sequence is then meaningless) and append
+ * leaves that sequence untouched.  Pools are addressed with 64-bit offsets
+ * (no 2 GiB limit).  Otherwise as msa_decode_fwd_varlen / msa_append_kv,
+ * with the same results for the same rows. */
+msa_status msa_decode_fwd_paged(const msa_decode_desc* desc, int32_t page_size, int32_t num_pages,
+                                const int32_t* block_table, const int32_t* ctx_lens, const void* q,
+                                const void* Kpages, const void* Vpages, const void* Kbar,
+                                const void* Vbar, void* workspace, size_t workspace_bytes, void* O,
+                                float* LSE, void* stream);
+
+msa_status msa_append_kv_paged(const msa_decode_desc* desc, int32_t page_size, int32_t num_pages,
+                               const int32_t* block_table, const int32_t* positions, const void* k_new,
+                               const void* v_new, void* Kpages, void* Vpages, void* Kbar, void* Vbar,
+                               void* stream);
 
 /* ---- Host-only introspection: the exact schedule the kernels use.  These
  * make no HIP call and need no GPU; all pointers are host memory. ---- */

@@ -32,6 +32,7 @@ EXPORTS = (
     "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_status_string",
     "msa_last_error", "msa_abi_version", "msa_decode_fwd_varlen", "msa_append_kv",
     "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd", "msa_attn_fwd_blocksparse",
+    "msa_decode_fwd_paged", "msa_append_kv_paged",
 )
 
 LIST_QUERY_BLOCK = 128
@@ -83,11 +84,13 @@ def lib() -> ctypes.CDLL:
         L.msa_plan_decode_varlen.argtypes = [P(DecodeDesc), i32, vp, P(i32), P(i32)]
         L.msa_attn_bwd_workspace_size.argtypes = [P(AttnDesc), P(sz)]
         L.msa_attn_fwd_blocksparse.argtypes = [P(AttnDesc), vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.msa_decode_fwd_paged.argtypes = [P(DecodeDesc), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.msa_append_kv_paged.argtypes = [P(DecodeDesc), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_attn_bwd.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         for f in ("msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
                   "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_decode_fwd_varlen",
                   "msa_append_kv", "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd",
-                  "msa_attn_fwd_blocksparse"):
+                  "msa_attn_fwd_blocksparse", "msa_decode_fwd_paged", "msa_append_kv_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -345,6 +348,57 @@ def msa_append_kv(k_new, v_new, positions, Kc, Vc, Kbar, Vbar, num_landmarks: in
     desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kc.dtype))
     _check(lib().msa_append_kv(ctypes.byref(desc), _ptr(positions), _ptr(k_new), _ptr(v_new), _ptr(Kc),
                                _ptr(Vc), _ptr(Kbar), _ptr(Vbar), _stream(Kc, stream)))
+
+
+def msa_decode_fwd_paged(q, Kpages, Vpages, block_table, Kbar, Vbar, ctx_lens, window: int, num_landmarks: int,
+                         num_splits: int, scale: Optional[float] = None, out_dtype=None, workspace=None, O=None,
+                         LSE=None, want_lse: bool = True, stream=None):
+    """Decode over paged caches: pools [num_pages][Hkv][page][d], block_table
+    int32 [B][pages per sequence] (capacity = pages per sequence x page)."""
+    import torch
+    B, Hq, d = q.shape
+    num_pages, Hkv, page, _ = Kpages.shape
+    if Vpages.shape != Kpages.shape or Kpages.shape[3] != d:
+        raise ValueError("page pools must be [num_pages][Hkv][page][d] and match q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B][pages per sequence]")
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
+    cap = block_table.shape[1] * page
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code)
+    need = msa_decode_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=_torch_dtype(out_code), device=q.device)
+    if LSE is None and want_lse:
+        LSE = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib().msa_decode_fwd_paged(ctypes.byref(desc), page, num_pages, _ptr(block_table), _ptr(ctx_lens),
+                                      _ptr(q), _ptr(Kpages), _ptr(Vpages), _ptr(Kbar), _ptr(Vbar), _ptr(workspace),
+                                      ws_bytes, _ptr(O), _ptr(LSE), _stream(q, stream)))
+    return O, LSE
+
+
+def msa_append_kv_paged(k_new, v_new, positions, Kpages, Vpages, block_table, Kbar, Vbar, num_landmarks: int,
+                        stream=None):
+    """msa_append_kv over paged caches (see msa_decode_fwd_paged)."""
+    import torch
+    num_pages, Hkv, page, d = Kpages.shape
+    B = block_table.shape[0]
+    if Vpages.shape != Kpages.shape or tuple(k_new.shape) != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new [B][Hkv][d] must match the page pools")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (B,):
+        raise ValueError("positions must be an int32 tensor of shape [B]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [B][pages per sequence]")
+    cap = block_table.shape[1] * page
+    desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kpages.dtype))
+    _check(lib().msa_append_kv_paged(ctypes.byref(desc), page, num_pages, _ptr(block_table), _ptr(positions),
+                                     _ptr(k_new), _ptr(v_new), _ptr(Kpages), _ptr(Vpages), _ptr(Kbar), _ptr(Vbar),
+                                     _stream(Kpages, stream)))
 
 
 def decode_partials(workspace, num_splits: int, batch: int, heads_q: int, head_dim: int):

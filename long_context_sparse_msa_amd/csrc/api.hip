@@ -84,7 +84,7 @@ msa_status check_attn(const msa_attn_desc* d) {
   return MSA_OK;
 }
 
-msa_status check_decode(const msa_decode_desc* d) {
+msa_status check_decode_shape(const msa_decode_desc* d) {
   if (d == nullptr) return fail(MSA_ERR_INVALID_ARG, "desc is NULL");
   if (d->batch < 0 || d->ctx_len < 1 || d->heads_kv < 1 || d->heads_q < 1 || d->heads_q % d->heads_kv != 0)
     return fail(MSA_ERR_INVALID_ARG,
@@ -108,8 +108,61 @@ msa_status check_decode(const msa_decode_desc* d) {
     return fail(MSA_ERR_INVALID_ARG, "out_dtype=%d is not a msa_dtype", d->out_dtype);
   const long long wgs = (long long)d->batch * d->heads_kv * d->num_splits;
   if (wgs > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MSA_OK;
+}
+
+// Contiguous caches additionally keep one head's cache under 2 GiB.
+msa_status check_decode(const msa_decode_desc* d) {
+  msa_status s = check_decode_shape(d);
+  if (s != MSA_OK) return s;
   if ((long long)d->ctx_len * d->head_dim * 2 >= (1LL << 31))
     return fail(MSA_ERR_UNSUPPORTED, "ctx_len=%d: one head's cache must be < 2 GiB", d->ctx_len);
+  return MSA_OK;
+}
+
+// Shape checks of the append entry points (the caches' layout is checked
+// by each caller).
+msa_status check_append_shape(const msa_decode_desc* desc) {
+  if (desc == nullptr) return fail(MSA_ERR_INVALID_ARG, "desc is NULL");
+  if (desc->batch < 0 || desc->ctx_len < 1 || desc->heads_kv < 1)
+    return fail(MSA_ERR_INVALID_ARG, "batch=%d ctx_len=%d heads_kv=%d: need batch>=0, ctx_len>=1, heads_kv>=1",
+                desc->batch, desc->ctx_len, desc->heads_kv);
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim=%d: supported values are 64 and 128", desc->head_dim);
+  if (desc->num_landmarks < 0 || (desc->num_landmarks > 0 && desc->ctx_len % desc->num_landmarks != 0))
+    return fail(MSA_ERR_INVALID_ARG, "num_landmarks=%d must be >= 0 and divide ctx_len=%d", desc->num_landmarks,
+                desc->ctx_len);
+  if (desc->in_dtype != MSA_DTYPE_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "the cache is bf16 only (in_dtype=%d)", desc->in_dtype);
+  if (2LL * desc->batch * desc->heads_kv > (1LL << 31) - 1)
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MSA_OK;
+}
+
+// Paging arguments shared by the paged entry points.
+msa_status check_paging(const msa_decode_desc* d, int32_t page_size, int32_t num_pages, const int32_t* table,
+                        msa::DecodePaging* out) {
+  if (page_size < 32 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "page_size=%d must be a power of two in [32, 2^20]", page_size);
+  if (d->ctx_len % page_size != 0)
+    return fail(MSA_ERR_INVALID_ARG, "ctx_len=%d (the capacity) must be a multiple of page_size=%d", d->ctx_len,
+                page_size);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%d must be >= 1", num_pages);
+  if (table == nullptr || (reinterpret_cast<uintptr_t>(table) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "block_table is NULL or not 4-byte aligned");
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  *out = msa::DecodePaging{table, shift, d->ctx_len / page_size, num_pages};
+  return MSA_OK;
+}
+
+msa_status check_bwd(const msa_attn_desc* d) {
+  msa_status s = check_attn(d);
+  if (s != MSA_OK) return s;
+  if (d->in_dtype != MSA_DTYPE_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "the backward takes bf16 inputs only (in_dtype=%d)", d->in_dtype);
+  const long long rows = (long long)d->batch * d->heads_q * (((long long)d->seq_len + 127) / 128 * 128);
+  if ((rows + 15) / 16 > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
   return MSA_OK;
 }
 
@@ -193,16 +246,6 @@ msa_status msa_attn_fwd_blocksparse(const msa_attn_desc* desc, const int32_t* bl
                     "block-sparse attention launch");
 }
 
-msa_status check_bwd(const msa_attn_desc* d) {
-  msa_status s = check_attn(d);
-  if (s != MSA_OK) return s;
-  if (d->in_dtype != MSA_DTYPE_BF16)
-    return fail(MSA_ERR_UNSUPPORTED, "the backward takes bf16 inputs only (in_dtype=%d)", d->in_dtype);
-  const long long rows = (long long)d->batch * d->heads_q * (((long long)d->seq_len + 127) / 128 * 128);
-  if ((rows + 15) / 16 > (1LL << 31) - 1) return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
-  return MSA_OK;
-}
-
 msa_status msa_attn_bwd_workspace_size(const msa_attn_desc* desc, size_t* bytes) {
   msa_status s = check_bwd(desc);
   if (s != MSA_OK) return s;
@@ -231,7 +274,7 @@ msa_status msa_attn_bwd(const msa_attn_desc* desc, const void* Q, const void* K,
 }
 
 msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes) {
-  msa_status s = check_decode(desc);
+  msa_status s = check_decode_shape(desc);  // the size does not depend on the caches' layout
   if (s != MSA_OK) return s;
   if (bytes == nullptr) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = decode_ws_bytes(desc);
@@ -254,7 +297,7 @@ msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void
     return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
-  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, nullptr, ws_o, ws_lse, O, LSE,
+  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, nullptr, nullptr, ws_o, ws_lse, O, LSE,
                                        static_cast<hipStream_t>(stream)),
                     "decode launch");
 }
@@ -278,28 +321,17 @@ msa_status msa_decode_fwd_varlen(const msa_decode_desc* desc, const int32_t* ctx
     return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
-  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, ctx_lens, ws_o, ws_lse, O, LSE,
+  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, ctx_lens, nullptr, ws_o, ws_lse, O, LSE,
                                        static_cast<hipStream_t>(stream)),
                     "decode launch");
 }
 
 msa_status msa_append_kv(const msa_decode_desc* desc, const int32_t* positions, const void* k_new,
                          const void* v_new, void* Kcache, void* Vcache, void* Kbar, void* Vbar, void* stream) {
-  if (desc == nullptr) return fail(MSA_ERR_INVALID_ARG, "desc is NULL");
-  if (desc->batch < 0 || desc->ctx_len < 1 || desc->heads_kv < 1)
-    return fail(MSA_ERR_INVALID_ARG, "batch=%d ctx_len=%d heads_kv=%d: need batch>=0, ctx_len>=1, heads_kv>=1",
-                desc->batch, desc->ctx_len, desc->heads_kv);
-  if (desc->head_dim != 64 && desc->head_dim != 128)
-    return fail(MSA_ERR_UNSUPPORTED, "head_dim=%d: supported values are 64 and 128", desc->head_dim);
-  if (desc->num_landmarks < 0 || (desc->num_landmarks > 0 && desc->ctx_len % desc->num_landmarks != 0))
-    return fail(MSA_ERR_INVALID_ARG, "num_landmarks=%d must be >= 0 and divide ctx_len=%d", desc->num_landmarks,
-                desc->ctx_len);
-  if (desc->in_dtype != MSA_DTYPE_BF16)
-    return fail(MSA_ERR_UNSUPPORTED, "the cache is bf16 only (in_dtype=%d)", desc->in_dtype);
+  msa_status s0 = check_append_shape(desc);
+  if (s0 != MSA_OK) return s0;
   if ((long long)desc->ctx_len * desc->head_dim * 2 >= (1LL << 31))
     return fail(MSA_ERR_UNSUPPORTED, "ctx_len=%d: one head's cache must be < 2 GiB", desc->ctx_len);
-  if (2LL * desc->batch * desc->heads_kv > (1LL << 31) - 1)
-    return fail(MSA_ERR_UNSUPPORTED, "problem too large for one launch");
   if (desc->batch == 0) return ok();
   if (positions == nullptr) return fail(MSA_ERR_INVALID_ARG, "positions is NULL");
   if ((reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
@@ -309,9 +341,55 @@ msa_status msa_append_kv(const msa_decode_desc* desc, const int32_t* positions, 
       (s = check_ptr(Vcache, "Vcache")))
     return s;
   if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
-  return hip_status(msa::launch_append(*desc, positions, k_new, v_new, Kcache, Vcache, Kbar, Vbar,
+  return hip_status(msa::launch_append(*desc, positions, nullptr, k_new, v_new, Kcache, Vcache, Kbar, Vbar,
                                        static_cast<hipStream_t>(stream)),
                     "append launch");
+}
+
+msa_status msa_decode_fwd_paged(const msa_decode_desc* desc, int32_t page_size, int32_t num_pages,
+                                const int32_t* block_table, const int32_t* ctx_lens, const void* q,
+                                const void* Kpages, const void* Vpages, const void* Kbar, const void* Vbar,
+                                void* workspace, size_t workspace_bytes, void* O, float* LSE, void* stream) {
+  msa_status s = check_decode_shape(desc);
+  if (s != MSA_OK) return s;
+  if (desc->batch == 0) return ok();
+  msa::DecodePaging pg;
+  if ((s = check_paging(desc, page_size, num_pages, block_table, &pg)) != MSA_OK) return s;
+  if (ctx_lens == nullptr || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "ctx_lens is NULL or not 4-byte aligned");
+  if ((s = check_ptr(q, "q")) || (s = check_ptr(Kpages, "Kpages")) || (s = check_ptr(Vpages, "Vpages")) ||
+      (s = check_ptr(O, "O")) || (s = check_ptr(workspace, "workspace")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  if (LSE != nullptr && !aligned16(LSE)) return fail(MSA_ERR_INVALID_ARG, "LSE is not 16-byte aligned");
+  const size_t need = decode_ws_bytes(desc);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
+  return hip_status(msa::launch_decode(*desc, q, Kpages, Vpages, Kbar, Vbar, ctx_lens, &pg, ws_o, ws_lse, O, LSE,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged decode launch");
+}
+
+msa_status msa_append_kv_paged(const msa_decode_desc* desc, int32_t page_size, int32_t num_pages,
+                               const int32_t* block_table, const int32_t* positions, const void* k_new,
+                               const void* v_new, void* Kpages, void* Vpages, void* Kbar, void* Vbar,
+                               void* stream) {
+  msa_status s = check_append_shape(desc);
+  if (s != MSA_OK) return s;
+  if (desc->batch == 0) return ok();
+  msa::DecodePaging pg;
+  if ((s = check_paging(desc, page_size, num_pages, block_table, &pg)) != MSA_OK) return s;
+  if (positions == nullptr || (reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
+    return fail(MSA_ERR_INVALID_ARG, "positions is NULL or not 4-byte aligned");
+  if ((s = check_ptr(k_new, "k_new")) || (s = check_ptr(v_new, "v_new")) || (s = check_ptr(Kpages, "Kpages")) ||
+      (s = check_ptr(Vpages, "Vpages")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  return hip_status(msa::launch_append(*desc, positions, &pg, k_new, v_new, Kpages, Vpages, Kbar, Vbar,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged append launch");
 }
 
 msa_status msa_plan_rows(const msa_attn_desc* desc, int32_t* win_lo, int32_t* lm_count) {

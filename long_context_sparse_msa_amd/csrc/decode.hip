@@ -80,22 +80,73 @@ struct Tile {
 // win0 + e - lm; rows past cnt repeat entry e0 (finite data that gets zero
 // weight).  (A device function rather than a lambda in the kernel: with the
 // load builtin inside a lambda the host pass drops the kernel's launch stub.)
+// Paged caches: the physical pages that this lane's rows of one tile lie
+// in (at most two, logical pages lpA <= lpA + 1, since a tile spans at most
+// 32 rows and pages hold at least 32), loaded one tile ahead.
+struct PageIds {
+  int lpA, idA, idB;
+};
+
+// With PAGED, window row r of the sequence lives at row (r mod page) of
+// physical page tbl[r / page]: kc/vc are then the pools' bases for this KV
+// head and pstride the bytes between consecutive physical pages of it.  A
+// page id outside [0, num_pages) reads page 0 (no access leaves the pool).
 template <int D, int TE>
 struct Stager {
   using T = Tile<D, TE>;
   const unsigned char *kl, *vl, *kc, *vc;
   int lm, win0, lane;
+  const int32_t* tbl;  // this sequence's block table (paged), else null
+  int shift, max_pages, num_pages;
+  size_t pstride;
 
-  __device__ __forceinline__ void issue(unsigned char* slot, int e0, int cnt) const {
+  __device__ __forceinline__ int entry(int e0, int cnt, int i) const {
+    const int r = (i * 64 + lane) / T::CH;
+    return e0 + (r < cnt ? r : 0);
+  }
+  // Page ids of this lane's window rows of the tile at e0 (vector loads).
+  __device__ __forceinline__ PageIds fetch(int e0, int cnt) const {
+    int lo = 0x7fffffff, hi = 0;
+#pragma unroll
+    for (int i = 0; i < T::KI; ++i) {
+      const int e = entry(e0, cnt, i);
+      if (e >= lm) {
+        const int row = win0 + e - lm;
+        lo = min(lo, row);
+        hi = max(hi, row);
+      }
+    }
+    PageIds pg;
+    pg.lpA = lo == 0x7fffffff ? 0 : lo >> shift;
+    const int lpB = hi >> shift;
+    pg.idA = tbl[min(pg.lpA, max_pages - 1)];
+    pg.idB = tbl[min(lpB, max_pages - 1)];
+    return pg;
+  }
+  template <bool PAGED>
+  __device__ __forceinline__ void issue(unsigned char* slot, int e0, int cnt, const PageIds& pg) const {
 #pragma unroll
     for (int i = 0; i < T::KI; ++i) {
       const int sl = i * 64 + lane;
       const int r = sl / T::CH, p = sl % T::CH;
-      const int e = e0 + (r < cnt ? r : 0);
+      const int e = entry(e0, cnt, i);
       const bool is_lm = e < lm;
-      const size_t row = is_lm ? (size_t)e : (size_t)(win0 + e - lm);
-      const unsigned char* ks = (is_lm ? kl : kc) + row * T::RB;
-      const unsigned char* vs = (is_lm ? vl : vc) + row * T::RB;
+      const unsigned char *ks, *vs;
+      if (is_lm) {
+        ks = kl + (size_t)e * T::RB;
+        vs = vl + (size_t)e * T::RB;
+      } else if constexpr (PAGED) {
+        const int row = win0 + e - lm;
+        int id = (row >> shift) == pg.lpA ? pg.idA : pg.idB;
+        id = (unsigned)id < (unsigned)num_pages ? id : 0;
+        const size_t off = (size_t)id * pstride + (size_t)(row & ((1 << shift) - 1)) * T::RB;
+        ks = kc + off;
+        vs = vc + off;
+      } else {
+        const size_t row = (size_t)(win0 + e - lm);
+        ks = kc + row * T::RB;
+        vs = vc + row * T::RB;
+      }
       __builtin_amdgcn_global_load_lds(ks + (p ^ T::kswz(r)) * 16, (lds_void_ptr)(slot + i * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vs + (p ^ T::vswz(r)) * 16, (lds_void_ptr)(slot + T::BYTES + i * 1024), 16,
                                        0, 0);
@@ -251,19 +302,40 @@ struct ChunkTiles {
 
 // Next tile to load of a wavefront that streams chunks [c, cend) tile by
 // tile into a two-slot ring.
+// With PAGED, pg holds the page ids of the tile about to be issued; after
+// issuing, the ids of the following tile are fetched into it (they land with
+// that tile's predecessor, before the wait that precedes its issue).
 struct IssueCursor {
   int c, t, n_issued;
-  template <int D, int TE>
+  template <bool PAGED, int D, int TE>
   __device__ __forceinline__ void next(const Stager<D, TE>& sg, const ChunkTiles<TE>& ct, unsigned char* ring,
-                                       int cend) {
+                                       int cend, PageIds& pg) {
     if (c >= cend) return;
     const int e0 = ct.lo(c) + t * TE;
-    sg.issue(ring + (n_issued & 1) * Tile<D, TE>::SLOT, e0, min(TE, ct.hi(c) - e0));
+    sg.template issue<PAGED>(ring + (n_issued & 1) * Tile<D, TE>::SLOT, e0, min(TE, ct.hi(c) - e0), pg);
     ++n_issued;
     if (++t == ct.ntile(c)) {
       ++c;
       t = 0;
     }
+    if constexpr (PAGED) {
+      if (c < cend) {
+        const int e1 = ct.lo(c) + t * TE;
+        pg = sg.fetch(e1, min(TE, ct.hi(c) - e1));
+      }
+    }
+  }
+  // Page ids of the cursor's current tile (the first one to issue).
+  template <bool PAGED, int D, int TE>
+  __device__ __forceinline__ PageIds first(const Stager<D, TE>& sg, const ChunkTiles<TE>& ct, int cend) const {
+    PageIds pg{0, 0, 0};
+    if constexpr (PAGED) {
+      if (c < cend) {
+        const int e0 = ct.lo(c) + t * TE;
+        pg = sg.fetch(e0, min(TE, ct.hi(c) - e0));
+      }
+    }
+    return pg;
   }
 };
 
@@ -277,6 +349,8 @@ struct DecodeArgs {
   int lm, win0, E, chunk, S;  // plan of row ctx-1 (used when lens is null)
   const int32_t* lens;     // per-sequence lengths, or null: every sequence holds ctx tokens
   int w, L;                // window and landmark block length (lens path)
+  const int32_t* table;    // paged caches: block table [B][max_pages], else null
+  int page_shift, max_pages, num_pages;
 };
 
 // Plan of sequence b: the static one, or that of its own length (clamped to
@@ -296,22 +370,37 @@ __device__ __forceinline__ DecodePlan seq_plan(const DecodeArgs& A, int b) {
   return decode_plan_fixed(n, A.w, A.G, A.L, A.S);
 }
 
-template <int D, int TE>
+template <bool PAGED, int D, int TE>
 __device__ __forceinline__ Stager<D, TE> make_stager(const DecodeArgs& A, int bk, int lane, const DecodePlan& p) {
-  const unsigned char* kc = reinterpret_cast<const unsigned char*>(A.Kc + (size_t)bk * A.ctx * D);
-  const unsigned char* vc = reinterpret_cast<const unsigned char*>(A.Vc + (size_t)bk * A.ctx * D);
+  const unsigned char* kc;
+  const unsigned char* vc;
+  const int32_t* tbl = nullptr;
+  size_t pstride = 0;
+  if constexpr (PAGED) {
+    // pools [num_pages][Hkv][page][D]: this KV head's rows of page id start
+    // at (id * Hkv + kvh) * page * D
+    const int kvh = bk % A.Hkv, b = bk / A.Hkv;
+    const size_t page_elems = (size_t)D << A.page_shift;
+    kc = reinterpret_cast<const unsigned char*>(A.Kc + (size_t)kvh * page_elems);
+    vc = reinterpret_cast<const unsigned char*>(A.Vc + (size_t)kvh * page_elems);
+    pstride = (size_t)A.Hkv * page_elems * 2;
+    tbl = A.table + (size_t)b * A.max_pages;
+  } else {
+    kc = reinterpret_cast<const unsigned char*>(A.Kc + (size_t)bk * A.ctx * D);
+    vc = reinterpret_cast<const unsigned char*>(A.Vc + (size_t)bk * A.ctx * D);
+  }
   const unsigned char* kl = kc;
   const unsigned char* vl = vc;
   if (A.G > 0) {
     kl = reinterpret_cast<const unsigned char*>(A.Kb + (size_t)bk * A.G * D);
     vl = reinterpret_cast<const unsigned char*>(A.Vb + (size_t)bk * A.G * D);
   }
-  return Stager<D, TE>{kl, vl, kc, vc, p.lm, p.win0, lane};
+  return Stager<D, TE>{kl, vl, kc, vc, p.lm, p.win0, lane, tbl, A.page_shift, A.max_pages, A.num_pages, pstride};
 }
 
 // ---------------------------------------------------------------------------
 // Split schedule, pass 1: one wavefront per (sequence, KV head, chunk).
-template <int D, int TE>
+template <int D, int TE, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs A) {
   using T = Tile<D, TE>;
   __shared__ __align__(16) unsigned char ring[T::RING];
@@ -325,18 +414,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs A) {
   const int e_beg = c * p.chunk;
   const int e_end = min(p.entries, e_beg + p.chunk);
   const int n_t = e_end > e_beg ? (e_end - e_beg + TE - 1) / TE : 0;
-  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane, p);
+  const Stager<D, TE> sg = make_stager<PAGED, D, TE>(A, bk, lane, p);
   WaveOps<D, TE> w;
   w.init(A.q + ((size_t)b * A.Hq + kvh * grp) * D, grp, c16, g4);
   Acc<D> a;
   a.reset();
 
-  if (n_t > 0) sg.issue(ring, e_beg, min(TE, e_end - e_beg));
+  // with PAGED, pg holds the page ids of the next tile to issue
+  PageIds pg{0, 0, 0};
+  if constexpr (PAGED) {
+    if (n_t > 0) pg = sg.fetch(e_beg, min(TE, e_end - e_beg));
+  }
+  if (n_t > 0) sg.template issue<PAGED>(ring, e_beg, min(TE, e_end - e_beg), pg);
+  if constexpr (PAGED) {
+    if (n_t > 1) pg = sg.fetch(e_beg + TE, min(TE, e_end - e_beg - TE));
+  }
   for (int t = 0; t < n_t; ++t) {
-    wait_vmcnt0();  // tile t is in LDS; tile t-1's slot was consumed in the previous step
+    wait_vmcnt0();  // tile t is in LDS (and tile t+1's page ids loaded); tile t-1's slot was consumed
     if (t + 1 < n_t) {
       const int e1 = e_beg + (t + 1) * TE;
-      sg.issue(ring + ((t + 1) & 1) * T::SLOT, e1, min(TE, e_end - e1));
+      sg.template issue<PAGED>(ring + ((t + 1) & 1) * T::SLOT, e1, min(TE, e_end - e1), pg);
+      if constexpr (PAGED) {
+        const int e2 = e1 + TE;
+        if (t + 2 < n_t) pg = sg.fetch(e2, min(TE, e_end - e2));
+      }
     }
     const int e0 = e_beg + t * TE;
     consume_tile<D, TE>(ring + (t & 1) * T::SLOT, min(TE, e_end - e0), w, A.c2, g4, a);
@@ -348,7 +449,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs A) {
 // ---------------------------------------------------------------------------
 // Fused schedule: one workgroup of kFusedWaves wavefronts per (sequence,
 // KV head); chunk partials, their merge and the final output in one pass.
-template <int D, int TE, bool OUT_BF16>
+template <int D, int TE, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(64 * kFusedWaves) void decode_fused_kernel(DecodeArgs A) {
   // (A.ws_o, A.ws_lse unused)
   using T = Tile<D, TE>;
@@ -370,7 +471,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_fused_kernel(DecodeAr
   const int cend = min(c1, n_ne);
   const ChunkTiles<TE> ct{p.chunk, p.entries};
 
-  const Stager<D, TE> sg = make_stager<D, TE>(A, bk, lane, p);
+  const Stager<D, TE> sg = make_stager<PAGED, D, TE>(A, bk, lane, p);
   WaveOps<D, TE> w;
   w.init(A.q + ((size_t)b * A.Hq + kvh * grp) * D, grp, c16, g4);
 
@@ -380,12 +481,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_fused_kernel(DecodeAr
   tot.reset();
   cur.reset();
   int n_used = 0;
-  cursor.next<D, TE>(sg, ct, ring, cend);
+  PageIds pg = cursor.first<PAGED, D, TE>(sg, ct, cend);
+  cursor.next<PAGED, D, TE>(sg, ct, ring, cend, pg);
   for (int c = c0; c < cend; ++c) {
     const int nt = ct.ntile(c);
     for (int t = 0; t < nt; ++t) {
-      wait_vmcnt0();  // this tile is in LDS; the other slot was consumed in the previous step
-      cursor.next<D, TE>(sg, ct, ring, cend);
+      wait_vmcnt0();  // this tile is in LDS (and the next tile's page ids); the other slot was consumed
+      cursor.next<PAGED, D, TE>(sg, ct, ring, cend, pg);
       const int e0 = ct.lo(c) + t * TE;
       consume_tile<D, TE>(ring + (n_used & 1) * T::SLOT, min(TE, ct.hi(c) - e0), w, A.c2, g4, cur);
       ++n_used;
@@ -529,28 +631,22 @@ bool use_fused(const msa_decode_desc& d) {
   return (long long)d.batch * d.heads_kv >= 2LL * device_cus() && d.num_splits >= kFusedWaves;
 }
 
-template <int D>
-hipError_t launch_t(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                    const void* Kb, const void* Vb, const int32_t* lens, float* ws_o, float* ws_lse, void* O,
-                    float* LSE, hipStream_t stream) {
-  const DecodePlan p = decode_plan(d.ctx_len, d.window, d.num_landmarks, d.num_splits);
-  const int L = d.num_landmarks > 0 ? d.ctx_len / d.num_landmarks : 1;
-  DecodeArgs A{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(Kc), static_cast<const uint16_t*>(Vc),
-               static_cast<const uint16_t*>(Kb), static_cast<const uint16_t*>(Vb), ws_o, ws_lse, O, LSE,
-               d.batch, d.heads_q, d.heads_kv, d.ctx_len, d.num_landmarks, d.scale * kLog2e, p.lm, p.win0,
-               p.entries, p.chunk, d.num_splits, lens, d.window, L};
+template <int D, bool PAGED>
+hipError_t launch_t(const msa_decode_desc& d, const DecodeArgs& A, float* ws_o, float* ws_lse, void* O, float* LSE,
+                    hipStream_t stream) {
   const long long pairs = (long long)d.batch * d.heads_kv;
   if (use_fused(d)) {
     if (d.out_dtype == MSA_DTYPE_BF16) {
-      hipLaunchKernelGGL((decode_fused_kernel<D, kFusedTE, true>), dim3((unsigned)pairs), dim3(64 * kFusedWaves), 0,
-                         stream, A);
+      hipLaunchKernelGGL((decode_fused_kernel<D, kFusedTE, true, PAGED>), dim3((unsigned)pairs),
+                         dim3(64 * kFusedWaves), 0, stream, A);
     } else {
-      hipLaunchKernelGGL((decode_fused_kernel<D, kFusedTE, false>), dim3((unsigned)pairs), dim3(64 * kFusedWaves), 0,
-                         stream, A);
+      hipLaunchKernelGGL((decode_fused_kernel<D, kFusedTE, false, PAGED>), dim3((unsigned)pairs),
+                         dim3(64 * kFusedWaves), 0, stream, A);
     }
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, kSplitTE>), dim3((unsigned)(pairs * d.num_splits)), dim3(64), 0, stream, A);
+  hipLaunchKernelGGL((decode_split_kernel<D, kSplitTE, PAGED>), dim3((unsigned)(pairs * d.num_splits)), dim3(64), 0,
+                     stream, A);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int BH = d.batch * d.heads_q;
@@ -568,10 +664,24 @@ hipError_t launch_t(const msa_decode_desc& d, const void* q, const void* Kc, con
 }  // namespace
 
 hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                         const void* Kbar, const void* Vbar, const int32_t* lens, float* ws_o, float* ws_lse,
-                         void* O, float* LSE, hipStream_t stream) {
-  return d.head_dim == 128 ? launch_t<128>(d, q, Kc, Vc, Kbar, Vbar, lens, ws_o, ws_lse, O, LSE, stream)
-                           : launch_t<64>(d, q, Kc, Vc, Kbar, Vbar, lens, ws_o, ws_lse, O, LSE, stream);
+                         const void* Kbar, const void* Vbar, const int32_t* lens, const DecodePaging* paging,
+                         float* ws_o, float* ws_lse, void* O, float* LSE, hipStream_t stream) {
+  const DecodePlan p = decode_plan(d.ctx_len, d.window, d.num_landmarks, d.num_splits);
+  const int L = d.num_landmarks > 0 ? d.ctx_len / d.num_landmarks : 1;
+  DecodeArgs A{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(Kc), static_cast<const uint16_t*>(Vc),
+               static_cast<const uint16_t*>(Kbar), static_cast<const uint16_t*>(Vbar), ws_o, ws_lse, O, LSE,
+               d.batch, d.heads_q, d.heads_kv, d.ctx_len, d.num_landmarks, d.scale * kLog2e, p.lm, p.win0,
+               p.entries, p.chunk, d.num_splits, lens, d.window, L, nullptr, 0, 0, 0};
+  if (paging != nullptr) {
+    A.table = paging->table;
+    A.page_shift = paging->page_shift;
+    A.max_pages = paging->max_pages;
+    A.num_pages = paging->num_pages;
+    return d.head_dim == 128 ? launch_t<128, true>(d, A, ws_o, ws_lse, O, LSE, stream)
+                             : launch_t<64, true>(d, A, ws_o, ws_lse, O, LSE, stream);
+  }
+  return d.head_dim == 128 ? launch_t<128, false>(d, A, ws_o, ws_lse, O, LSE, stream)
+                           : launch_t<64, false>(d, A, ws_o, ws_lse, O, LSE, stream);
 }
 
 }  // namespace msa

@@ -37,14 +37,23 @@ hipError_t launch_attn_bwd(const msa_attn_desc& d, const void* Q, const void* K,
                            const void* Vbar, const void* O, const float* LSE, const void* dO, void* workspace,
                            void* dQ, void* dK, void* dV, hipStream_t stream);
 
-// lens: per-sequence lengths in device memory, or null for ctx_len each.
+// Paged caches: pools [num_pages][Hkv][1 << page_shift][d]; sequence b's
+// logical page p is physical page table[b * max_pages + p].
+struct DecodePaging {
+  const int32_t* table;
+  int page_shift, max_pages, num_pages;
+};
+
+// lens: per-sequence lengths in device memory, or null for ctx_len each;
+// paging: null for contiguous caches [B][Hkv][ctx_len][d].
 hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc, const void* Vc,
-                         const void* Kbar, const void* Vbar, const int32_t* lens, float* ws_o, float* ws_lse,
-                         void* O, float* LSE, hipStream_t stream);
+                         const void* Kbar, const void* Vbar, const int32_t* lens, const DecodePaging* paging,
+                         float* ws_o, float* ws_lse, void* O, float* LSE, hipStream_t stream);
 
 // Write one token's K/V row per sequence at positions[b] (skipped outside
 // [0, ctx_len)) and re-pool the landmark block that row completes.
-hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
-                         const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar, hipStream_t stream);
+hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const DecodePaging* paging,
+                         const void* k_new, const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar,
+                         hipStream_t stream);
 
 }  // namespace msa

@@ -62,9 +62,31 @@ struct PoolShape {
   static constexpr int kRowLanes = 256 / kChunks;
 };
 
-template <typename T, int D, bool LAST>
-__device__ __forceinline__ void pool_block(const T* __restrict__ src, const T* __restrict__ last, int L,
-                                           T* __restrict__ dst, float (*red)[D + 1]) {
+// Rows of one block: consecutive rows from base, or rows row0 + r of a
+// paged cache looked up in a block table (an invalid page id reads page 0).
+template <typename T, int D>
+struct RowsContig {
+  const T* base;
+  __device__ __forceinline__ const T* row(int r) const { return base + (size_t)r * D; }
+};
+
+template <int D>
+struct RowsPaged {
+  const uint16_t* pool;  // this KV head's rows of physical page 0
+  const int32_t* tbl;    // this sequence's block table
+  size_t pstride;        // elements between consecutive physical pages of the KV head
+  int row0, shift, max_pages, num_pages;
+  __device__ __forceinline__ const uint16_t* row(int r) const {
+    const int g = row0 + r;
+    int id = tbl[min(g >> shift, max_pages - 1)];
+    id = (unsigned)id < (unsigned)num_pages ? id : 0;
+    return pool + (size_t)id * pstride + (size_t)(g & ((1 << shift) - 1)) * D;
+  }
+};
+
+template <typename T, int D, bool LAST, typename Rows>
+__device__ __forceinline__ void pool_block(const Rows& rows, const T* __restrict__ last, int L, T* __restrict__ dst,
+                                           float (*red)[D + 1]) {
   using PS = PoolShape<T, D>;
   constexpr int kE = PS::kE, kChunks = PS::kChunks, kRowLanes = PS::kRowLanes;
   const int ch = threadIdx.x % kChunks;
@@ -73,10 +95,10 @@ __device__ __forceinline__ void pool_block(const T* __restrict__ src, const T* _
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
 
-  const u32x4* p = reinterpret_cast<const u32x4*>(src) + ch;
   const u32x4* lp = reinterpret_cast<const u32x4*>(last) + ch;
-  constexpr int kStride = kChunks;  // u32x4 per row
-  auto row = [&](int r) -> const u32x4* { return (LAST && r == L - 1) ? lp : p + (size_t)r * kStride; };
+  auto row = [&](int r) -> const u32x4* {
+    return (LAST && r == L - 1) ? lp : reinterpret_cast<const u32x4*>(rows.row(r)) + ch;
+  };
   int r = rl;
   for (; r + 3 * kRowLanes < L; r += 4 * kRowLanes) {
     const u32x4 a = *row(r);
@@ -118,7 +140,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, cons
   const int lm = blk - bh * G;
   const T* src = (is_v ? V : K) + ((size_t)bh * n + (size_t)lm * L) * D;
   T* dst = (is_v ? Vbar : Kbar) + (size_t)blk * D;
-  pool_block<T, D, false>(src, nullptr, L, dst, red);
+  pool_block<T, D, false>(RowsContig<T, D>{src}, nullptr, L, dst, red);
 }
 
 // Append: one workgroup per (tensor, batch*kv_head).  The sequence's new
@@ -126,28 +148,57 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, cons
 // blk = (pos+1)/L - 1, that block's landmark is pooled again (rows before
 // pos from the cache, row pos from the new token).  A position outside
 // [0, C) leaves the sequence untouched.
+//
+// Paged caches (table != null): pools [num_pages][Hkv][page][D]; row pos of
+// sequence b lives at row pos mod page of physical page table[b][pos/page].
+// A sequence whose page id for pos lies outside [0, num_pages) is left
+// untouched (nothing is written); rows of the pooled block are looked up
+// one by one.
+struct AppendArgs {
+  const int32_t* positions;
+  const uint16_t *k_new, *v_new;
+  uint16_t *Kc, *Vc, *Kbar, *Vbar;
+  int Hkv, C, G, L, pairs;
+  const int32_t* table;
+  int shift, max_pages, num_pages;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void append_kernel(const int32_t* __restrict__ positions,
-                                                     const uint16_t* __restrict__ k_new,
-                                                     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ Kc,
-                                                     uint16_t* __restrict__ Vc, uint16_t* __restrict__ Kbar,
-                                                     uint16_t* __restrict__ Vbar, int Hkv, int C, int G, int L,
-                                                     int pairs) {
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs A) {
   __shared__ float red[PoolShape<uint16_t, D>::kRowLanes][D + 1];
   const int wg = blockIdx.x;
-  const bool is_v = wg >= pairs;
-  const int bk = is_v ? wg - pairs : wg;  // b * Hkv + kvh
-  const int pos = positions[bk / Hkv];
-  if (pos < 0 || pos >= C) return;
-  const uint16_t* src = (is_v ? v_new : k_new) + (size_t)bk * D;
-  uint16_t* cache = (is_v ? Vc : Kc) + (size_t)bk * C * D;
-  if (threadIdx.x < D / 8) {
-    reinterpret_cast<u32x4*>(cache + (size_t)pos * D)[threadIdx.x] = reinterpret_cast<const u32x4*>(src)[threadIdx.x];
+  const bool is_v = wg >= A.pairs;
+  const int bk = is_v ? wg - A.pairs : wg;  // b * Hkv + kvh
+  const int b = bk / A.Hkv, kvh = bk % A.Hkv;
+  const int pos = A.positions[b];
+  if (pos < 0 || pos >= A.C) return;
+  const uint16_t* src = (is_v ? A.v_new : A.k_new) + (size_t)bk * D;
+  uint16_t* dst_row;
+  RowsPaged<D> paged{};
+  if (A.table != nullptr) {
+    const size_t page_elems = (size_t)D << A.shift;
+    paged = RowsPaged<D>{(is_v ? A.Vc : A.Kc) + (size_t)kvh * page_elems, A.table + (size_t)b * A.max_pages,
+                         (size_t)A.Hkv * page_elems, 0, A.shift, A.max_pages, A.num_pages};
+    const int id = paged.tbl[pos >> A.shift];
+    if ((unsigned)id >= (unsigned)A.num_pages) return;
+    dst_row = const_cast<uint16_t*>(paged.pool) + (size_t)id * paged.pstride +
+              (size_t)(pos & ((1 << A.shift) - 1)) * D;
+  } else {
+    dst_row = (is_v ? A.Vc : A.Kc) + ((size_t)bk * A.C + pos) * D;
   }
-  if (G > 0 && (pos + 1) % L == 0) {
-    const int blk = (pos + 1) / L - 1;
-    uint16_t* dst = (is_v ? Vbar : Kbar) + ((size_t)bk * G + blk) * D;
-    pool_block<uint16_t, D, true>(cache + (size_t)blk * L * D, src, L, dst, red);
+  if (threadIdx.x < D / 8) {
+    reinterpret_cast<u32x4*>(dst_row)[threadIdx.x] = reinterpret_cast<const u32x4*>(src)[threadIdx.x];
+  }
+  if (A.G > 0 && (pos + 1) % A.L == 0) {
+    const int blk = (pos + 1) / A.L - 1;
+    uint16_t* dst = (is_v ? A.Vbar : A.Kbar) + ((size_t)bk * A.G + blk) * D;
+    if (A.table != nullptr) {
+      paged.row0 = blk * A.L;
+      pool_block<uint16_t, D, true>(paged, src, A.L, dst, red);
+    } else {
+      const uint16_t* cache = (is_v ? A.Vc : A.Kc) + (size_t)bk * A.C * D;
+      pool_block<uint16_t, D, true>(RowsContig<uint16_t, D>{cache + (size_t)blk * A.L * D}, src, A.L, dst, red);
+    }
   }
 }
 
@@ -163,25 +214,28 @@ hipError_t launch_pool_t(const msa_attn_desc& d, const void* K, const void* V, v
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_append_t(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
-                           const void* v_new, void* Kc, void* Vc, void* Kb, void* Vb, hipStream_t stream) {
-  const int G = d.num_landmarks;
-  const int L = G > 0 ? d.ctx_len / G : 1;
-  const int pairs = d.batch * d.heads_kv;
-  hipLaunchKernelGGL((append_kernel<D>), dim3(2 * pairs), dim3(256), 0, stream, positions,
-                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                     static_cast<uint16_t*>(Kc), static_cast<uint16_t*>(Vc), static_cast<uint16_t*>(Kb),
-                     static_cast<uint16_t*>(Vb), d.heads_kv, d.ctx_len, G, L, pairs);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const void* k_new,
-                         const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar, hipStream_t stream) {
-  return d.head_dim == 128 ? launch_append_t<128>(d, positions, k_new, v_new, Kc, Vc, Kbar, Vbar, stream)
-                           : launch_append_t<64>(d, positions, k_new, v_new, Kc, Vc, Kbar, Vbar, stream);
+hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const DecodePaging* paging,
+                         const void* k_new, const void* v_new, void* Kc, void* Vc, void* Kbar, void* Vbar,
+                         hipStream_t stream) {
+  const int G = d.num_landmarks;
+  AppendArgs A{positions, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+               static_cast<uint16_t*>(Kc), static_cast<uint16_t*>(Vc), static_cast<uint16_t*>(Kbar),
+               static_cast<uint16_t*>(Vbar), d.heads_kv, d.ctx_len, G, G > 0 ? d.ctx_len / G : 1,
+               d.batch * d.heads_kv, nullptr, 0, 0, 0};
+  if (paging != nullptr) {
+    A.table = paging->table;
+    A.shift = paging->page_shift;
+    A.max_pages = paging->max_pages;
+    A.num_pages = paging->num_pages;
+  }
+  if (d.head_dim == 128) {
+    hipLaunchKernelGGL((append_kernel<128>), dim3(2 * A.pairs), dim3(256), 0, stream, A);
+  } else {
+    hipLaunchKernelGGL((append_kernel<64>), dim3(2 * A.pairs), dim3(256), 0, stream, A);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_pool(const msa_attn_desc& d, const void* K, const void* V, void* Kbar, void* Vbar,

@@ -722,3 +722,23 @@ def attn_blocksparse_rows(Q, K, V, counts, indices, bq: int, bk: int, causal: bo
                 LSE[b, k] = m + np.log(p.sum())
         out[h] = (r_all, O, LSE)
     return out
+
+
+
+def gather_pages(pool, table, page: int):
+    """Contiguous caches [B, Hkv, P*page, d] of paged ones: pool
+    [num_pages, Hkv, page, d], table [B, P] (logical page -> physical page).
+    Entries outside [0, num_pages) give zero rows.  (The paged layout of the
+    "Sparse Attention GPU Cluster Implementation" page's FAQ mention of
+    PagedAttention; decode over it is decode_varlen over these caches.)"""
+    pool = np.asarray(pool, np.float64)
+    table = np.asarray(table)
+    B, P = table.shape
+    Hkv, d = pool.shape[1], pool.shape[3]
+    out = np.zeros((B, Hkv, P * page, d))
+    for b in range(B):
+        for lp in range(P):
+            pid = int(table[b, lp])
+            if 0 <= pid < pool.shape[0]:
+                out[b, :, lp * page:(lp + 1) * page] = pool[pid]
+    return out

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     assert sorted(msa.EXPORTS) == names
     for name in names:
         assert hasattr(L, name), name
@@ -354,3 +354,48 @@ def test_blocksparse_argument_checks():
     assert b"LSE" in msa.lib().msa_last_error()         # it fails on the LSE check that comes after
     assert call_list(d, ptr=24) == 1
     assert call_list(base_desc(batch=0), counts=None, idx=None, ptr=0) == 0
+
+
+# ---------------------------------------------------------- paged caches
+
+def call_paged(desc, page=64, num_pages=8, table=16, lens=16, lse=20):
+    # LSE misaligned by default: a call passing every other check still fails
+    # validation, so nothing is launched
+    p = ctypes.c_void_p(16)
+    t = None if table is None else ctypes.c_void_p(table)
+    ln = None if lens is None else ctypes.c_void_p(lens)
+    return msa.lib().msa_decode_fwd_paged(ctypes.byref(desc), page, num_pages, t, ln, p, p, p, p, p, p, 1 << 30,
+                                          p, ctypes.c_void_p(lse), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=16), 1), (dict(page=48), 1), (dict(page=1024), 1), (dict(num_pages=0), 1),
+    (dict(table=None), 1), (dict(table=18), 1), (dict(lens=None), 1), (dict(lens=22), 1),
+])
+def test_paged_decode_validation(kw, status):
+    d = dec_desc(ctx_len=512, num_landmarks=8)   # capacity 512: page 1024 does not divide it
+    assert call_paged(d, **kw) == status
+
+
+def test_paged_decode_passes_to_the_last_check():
+    d = dec_desc(ctx_len=512, num_landmarks=8)
+    assert call_paged(d) == 1 and b"LSE" in msa.lib().msa_last_error()
+    # pools are addressed in 64 bits: a capacity over 2 GiB per head is accepted
+    big = dec_desc(ctx_len=1 << 23, num_landmarks=8)
+    assert call_paged(big, page=1 << 16) == 1 and b"LSE" in msa.lib().msa_last_error()
+    # a contiguous decode of that capacity is refused
+    p = ctypes.c_void_p(16)
+    assert msa.lib().msa_decode_fwd(ctypes.byref(big), p, p, p, p, p, p, 1 << 30, p, None, None) == 2
+
+
+def test_paged_append_validation():
+    d = dec_desc(ctx_len=512, num_landmarks=8)
+    p = ctypes.c_void_p(16)
+    f = msa.lib().msa_append_kv_paged
+    assert f(ctypes.byref(d), 48, 8, p, p, p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), 64, 0, p, p, p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), 64, 8, None, p, p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), 64, 8, p, None, p, p, p, p, p, p, None) == 1
+    assert f(ctypes.byref(d), 64, 8, p, p, p, p, p, p, None, p, None) == 1   # Kbar needed with G > 0
+    assert f(ctypes.byref(dec_desc(in_dtype=msa.MSA_DTYPE_F32)), 64, 8, p, p, p, p, p, p, p, p, None) == 2
+    assert f(ctypes.byref(dec_desc(batch=0)), 48, 0, None, None, None, None, None, None, None, None, None) == 0

@@ -183,3 +183,85 @@ def test_append_then_decode(d, schedule, monkeypatch):
         for blk in range(lens[b] // L):
             exact = k_ref[b, :, blk * L:(blk + 1) * L].mean(axis=1)
             np.testing.assert_allclose(host64(Kb[b, :, blk]), exact, atol=2 ** -8 * np.abs(exact).max() + 1e-6)
+
+
+# ------------------------------------------------------------------ paged caches
+
+def to_pages(Kc, Vc, page, seed, extra=3):
+    """Scatter contiguous caches [B][Hkv][C][d] into page pools under a
+    seeded random permutation; `extra` pool pages are unused and hold large
+    values.  Returns (Kpages, Vpages, table int32 [B][C/page] on the device,
+    table as numpy)."""
+    B, Hkv, C, d = Kc.shape
+    P = C // page
+    n_pages = B * P + extra
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * P].reshape(B, P).astype(np.int32)
+    Kp = rand((n_pages, Hkv, page, d), seed) * 50
+    Vp = rand((n_pages, Hkv, page, d), seed + 1) * 50
+    for b in range(B):
+        for lp in range(P):
+            Kp[int(perm[b, lp])] = Kc[b, :, lp * page:(lp + 1) * page]
+            Vp[int(perm[b, lp])] = Vc[b, :, lp * page:(lp + 1) * page]
+    return Kp, Vp, torch.from_numpy(perm).to(dev()), perm
+
+
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("page", [32, 64, 256])
+def test_paged_decode_equals_contiguous(page, schedule, monkeypatch):
+    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+    B, Hq, Hkv, C, d, w, G, S, lens = VARLEN[0]
+    print(f"[case] paged decode {schedule} page={page} B={B} C={C} lens={lens}", flush=True)
+    q = rand((B, Hq, d), 61)
+    Kc, Vc = rand((B, Hkv, C, d), 62), rand((B, Hkv, C, d), 63)
+    poison_tail(Kc, Vc, lens)
+    Kb, Vb = msa.msa_pool_landmarks(Kc, Vc, G)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
+    Kp, Vp, table, perm = to_pages(Kc, Vc, page, 64 + page)
+    scale = 1.0 / math.sqrt(d)
+    Oc, Lc = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
+    Op, Lp = msa.msa_decode_fwd_paged(q, Kp, Vp, table, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # same rows, same tiles, same order: the same bits
+    assert torch.equal(Op, Oc) and torch.equal(Lp, Lc)
+    # and against the oracle over the gathered pools
+    k64 = orc.gather_pages(host64(Kp), perm, page)
+    v64 = orc.gather_pages(host64(Vp), perm, page)
+    o_ref, l_ref = orc.decode_varlen(host64(q), k64, v64, lens, w, C // G, G, scale)
+    live = np.array(lens) > 0
+    assert_close(host64(Op)[live], host64(Lp)[live], o_ref[live], l_ref[live], TOL_BF16, f"paged page={page}")
+
+
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+def test_paged_append_then_decode_equals_contiguous(schedule, monkeypatch):
+    """The append + decode sequence of test_append_then_decode on paged caches
+    gives the bits of the contiguous run at every step."""
+    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+    B, Hq, Hkv, C, d, w, G, S, steps, page = 4, 8, 2, 1024, 128, 40, 64, 6, 40, 32
+    L = C // G
+    print(f"[case] paged append+decode {schedule} page={page} steps={steps}", flush=True)
+    start = [0, 100, 1000, 31]
+    idle = [False, True, False, False]
+    Kc, Vc = rand((B, Hkv, C, d), 71), rand((B, Hkv, C, d), 72)
+    poison_tail(Kc, Vc, start)
+    Kb, Vb = msa.msa_pool_landmarks(Kc, Vc, G)
+    Kp, Vp, table, perm = to_pages(Kc, Vc, page, 73)
+    Kbp, Vbp = Kb.clone(), Vb.clone()
+    k_new, v_new = rand((steps, B, Hkv, d), 74), rand((steps, B, Hkv, d), 75)
+    qs = rand((steps, B, Hq, d), 76)
+    lens = list(start)
+    for t in range(steps):
+        pos = torch.tensor([-1 if idle[b] else lens[b] for b in range(B)], dtype=torch.int32, device=dev())
+        msa.msa_append_kv(k_new[t], v_new[t], pos, Kc, Vc, Kb, Vb, G)
+        msa.msa_append_kv_paged(k_new[t], v_new[t], pos, Kp, Vp, table, Kbp, Vbp, G)
+        lens = [min(C, lens[b] + 1) if not idle[b] else lens[b] for b in range(B)]
+        lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
+        Oc, Lc = msa.msa_decode_fwd_varlen(qs[t], Kc, Vc, Kb, Vb, lens_d, w, G, S, out_dtype=torch.float32)
+        Op, Lp = msa.msa_decode_fwd_paged(qs[t], Kp, Vp, table, Kbp, Vbp, lens_d, w, G, S, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(Op, Oc) and torch.equal(Lp, Lc), t
+    assert torch.equal(Kbp, Kb) and torch.equal(Vbp, Vb)
+    # every row the paged appends wrote sits where the table says
+    gathered = orc.gather_pages(host64(Kp), perm, page)
+    np.testing.assert_array_equal(gathered, host64(Kc))
+    gathered = orc.gather_pages(host64(Vp), perm, page)
+    np.testing.assert_array_equal(gathered, host64(Vc))

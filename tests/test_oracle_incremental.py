@@ -182,3 +182,21 @@ def test_append_then_decode_equals_decode_of_the_whole_prefix():
         Op, Lp = orc.attn_dense(Qp, Kp, Vp, w, m // L, SC)
         np.testing.assert_allclose(O, Op[:, :, t], atol=1e-12)
         np.testing.assert_allclose(LSE, Lp[:, :, t], atol=1e-12)
+
+
+# ---------------------------------------------------------------- paging
+
+def test_gather_pages_inverts_a_scatter():
+    rng = np.random.default_rng(460)
+    B, Hkv, P, page, d = 3, 2, 5, 4, 3
+    X = rng.standard_normal((B, Hkv, P * page, d))
+    perm = rng.permutation(B * P + 4)[:B * P].reshape(B, P)   # 4 pool pages stay unused
+    pool = rng.standard_normal((B * P + 4, Hkv, page, d))
+    for b in range(B):
+        for lp in range(P):
+            pool[perm[b, lp]] = X[b, :, lp * page:(lp + 1) * page]
+    np.testing.assert_array_equal(orc.gather_pages(pool, perm, page), X)
+    bad = perm.copy()
+    bad[1, 2] = -1
+    g = orc.gather_pages(pool, bad, page)
+    assert (g[1, :, 8:12] == 0).all()
