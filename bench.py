@@ -422,7 +422,7 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 
