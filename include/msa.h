@@ -71,6 +71,10 @@ typedef enum {
 
 typedef enum { MSA_DTYPE_F32 = 0, MSA_DTYPE_BF16 = 1 } msa_dtype;
 
+/* Decode schedule (see msa_decode_fwd): chosen from the problem's shape, or
+ * forced. */
+typedef enum { MSA_DECODE_AUTO = 0, MSA_DECODE_SPLIT = 1, MSA_DECODE_FUSED = 2 } msa_decode_schedule;
+
 /* Prefill problem.  head_dim in {64, 128}.  window >= 1 (a window >= n is
  * plain causal attention).  num_landmarks G >= 0; G > 0 requires n % G == 0.
  * in_dtype is the dtype of Q, K, V, Kbar, Vbar; out_dtype that of O
@@ -106,6 +110,7 @@ typedef struct {
   float scale; /* finite and > 0 */
   int32_t in_dtype;
   int32_t out_dtype;
+  int32_t schedule; /* msa_decode_schedule */
 } msa_decode_desc;
 
 /* Landmark pooling.  Reads K, V [B][Hkv][n][d] (n = desc->seq_len) and
@@ -209,9 +214,10 @@ msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes)
  *    and a second kernel merges them;
  *  - fused: one workgroup per (sequence, KV head) streams all its chunks,
  *    merging the partials on chip; the workspace is not written.
- * The fused schedule is used when batch*heads_kv >= 2 x (compute units) and
- * num_splits >= 4; the environment variable MSA_DECODE_SCHEDULE=split|fused,
- * read at each call, forces one of them.
+ * With schedule = MSA_DECODE_AUTO the fused schedule is used when
+ * batch*heads_kv >= 2 x (compute units) and num_splits >= 4;
+ * MSA_DECODE_SPLIT or MSA_DECODE_FUSED forces one of them (any other value:
+ * MSA_ERR_INVALID_ARG).
  * The workspace is caller-owned scratch of at least
  * msa_decode_workspace_size() bytes (required by both schedules).
  * Kbar/Vbar: landmarks of the caches (NULL if G == 0).  LSE may be NULL.
@@ -238,8 +244,8 @@ msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void
  * array [B], 4-byte aligned): its query, at position n_b-1, sees the window
  * keys n_b-w .. n_b-1 and the landmarks b' with (b'+1)*L - 1 <= n_b-1-w.
  * Its visible list is chunked, computed and merged exactly as in
- * msa_decode_fwd (same schedules, same workspace size and layout, same
- * MSA_DECODE_SCHEDULE override).  Only rows < n_b of the caches and
+ * msa_decode_fwd (same schedules and schedule field, same workspace size and
+ * layout).  Only rows < n_b of the caches and
  * landmark slots < (n_b - w)/L are read.  n_b is clamped to [0, C] on the
  * device (the host cannot read it); n_b = 0 gives O = 0 and LSE = -inf.
  * With every n_b = C this is msa_decode_fwd.  Other arguments and errors as

@@ -5,6 +5,9 @@ under csrc/); this package is its thin Python binding.
 """
 from .binding import (  # noqa: F401
     EXPORTS,
+    MSA_DECODE_AUTO,
+    MSA_DECODE_FUSED,
+    MSA_DECODE_SPLIT,
     MSA_DTYPE_BF16,
     MSA_DTYPE_F32,
     AttnDesc,

@@ -56,7 +56,22 @@ class DecodeDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("ctx_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("num_landmarks", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
+
+
+MSA_DECODE_AUTO = 0
+MSA_DECODE_SPLIT = 1
+MSA_DECODE_FUSED = 2
+_SCHEDULES = {None: MSA_DECODE_AUTO, "auto": MSA_DECODE_AUTO, "split": MSA_DECODE_SPLIT, "fused": MSA_DECODE_FUSED}
+
+
+def _schedule_code(schedule) -> int:
+    if isinstance(schedule, int):
+        return schedule
+    if schedule not in _SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(k for k in _SCHEDULES if k)} (got {schedule!r})")
+    return _SCHEDULES[schedule]
 
 
 _lib = None
@@ -150,13 +165,13 @@ def attn_desc(batch, heads_q, heads_kv, seq_len, head_dim, window, num_landmarks
 
 
 def decode_desc(batch, heads_q, heads_kv, ctx_len, head_dim, window, num_landmarks, num_splits,
-                scale=None, in_dtype=MSA_DTYPE_BF16, out_dtype=None) -> DecodeDesc:
+                scale=None, in_dtype=MSA_DTYPE_BF16, out_dtype=None, schedule=None) -> DecodeDesc:
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     if out_dtype is None:
         out_dtype = in_dtype
     return DecodeDesc(batch, heads_q, heads_kv, ctx_len, head_dim, window, num_landmarks, num_splits,
-                      scale, in_dtype, out_dtype)
+                      scale, in_dtype, out_dtype, _schedule_code(schedule))
 
 
 # ---------------------------------------------------------------- compute
@@ -277,7 +292,7 @@ def msa_decode_workspace_size(desc: DecodeDesc) -> int:
 
 def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_splits: int,
                    scale: Optional[float] = None, out_dtype=None, workspace=None, O=None, LSE=None,
-                   want_lse: bool = True, stream=None):
+                   want_lse: bool = True, stream=None, schedule=None):
     """Decode for the query at position ctx-1: (O [B][Hq][d], LSE [B][Hq]).
     ``workspace`` (uint8 or float32 device tensor) receives the per-chunk
     partials; it is allocated here when not given."""
@@ -288,7 +303,7 @@ def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_s
         raise ValueError("cache shapes do not match q")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
-    desc = decode_desc(B, Hq, Hkv, ctx, d, window, num_landmarks, num_splits, scale, in_code, out_code)
+    desc = decode_desc(B, Hq, Hkv, ctx, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
@@ -304,7 +319,7 @@ def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_s
 
 def msa_decode_fwd_varlen(q, Kc, Vc, Kbar, Vbar, ctx_lens, window: int, num_landmarks: int,
                           num_splits: int, scale: Optional[float] = None, out_dtype=None, workspace=None,
-                          O=None, LSE=None, want_lse: bool = True, stream=None):
+                          O=None, LSE=None, want_lse: bool = True, stream=None, schedule=None):
     """Decode of sequences of different lengths: sequence b holds
     ctx_lens[b] tokens (int32 device tensor [B]) of a cache with capacity
     Kc.shape[2] rows; its query is at position ctx_lens[b]-1.  Landmark
@@ -318,7 +333,7 @@ def msa_decode_fwd_varlen(q, Kc, Vc, Kbar, Vbar, ctx_lens, window: int, num_land
         raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
-    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code)
+    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
@@ -352,7 +367,7 @@ def msa_append_kv(k_new, v_new, positions, Kc, Vc, Kbar, Vbar, num_landmarks: in
 
 def msa_decode_fwd_paged(q, Kpages, Vpages, block_table, Kbar, Vbar, ctx_lens, window: int, num_landmarks: int,
                          num_splits: int, scale: Optional[float] = None, out_dtype=None, workspace=None, O=None,
-                         LSE=None, want_lse: bool = True, stream=None):
+                         LSE=None, want_lse: bool = True, stream=None, schedule=None):
     """Decode over paged caches: pools [num_pages][Hkv][page][d], block_table
     int32 [B][pages per sequence] (capacity = pages per sequence x page)."""
     import torch
@@ -367,7 +382,7 @@ def msa_decode_fwd_paged(q, Kpages, Vpages, block_table, Kbar, Vbar, ctx_lens, w
     cap = block_table.shape[1] * page
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
-    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code)
+    desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)

@@ -100,6 +100,8 @@ msa_status check_decode_shape(const msa_decode_desc* d) {
     return fail(MSA_ERR_INVALID_ARG, "num_landmarks=%d must be >= 0 and divide ctx_len=%d", d->num_landmarks,
                 d->ctx_len);
   if (d->num_splits < 1) return fail(MSA_ERR_INVALID_ARG, "num_splits=%d must be >= 1", d->num_splits);
+  if (d->schedule != MSA_DECODE_AUTO && d->schedule != MSA_DECODE_SPLIT && d->schedule != MSA_DECODE_FUSED)
+    return fail(MSA_ERR_INVALID_ARG, "schedule=%d is not a msa_decode_schedule", d->schedule);
   if (!isfinite(d->scale) || !(d->scale > 0.f))
     return fail(MSA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (d->in_dtype != MSA_DTYPE_BF16)

@@ -29,9 +29,6 @@
 //  * split (few pairs, where chunks are the parallelism): one wavefront per
 //    (sequence, KV head, chunk) writes its partial; decode_merge_kernel
 //    then merges the chunks of each (sequence, query head).
-#include <cstdlib>
-#include <cstring>
-
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 #include "msa_plan.hpp"
@@ -622,12 +619,11 @@ int device_cus() {
 }
 
 // The fused schedule needs enough (sequence, KV head) pairs to fill the
-// chip with one workgroup each and at least one chunk per wavefront;
-// MSA_DECODE_SCHEDULE=split|fused overrides the choice.
+// chip with one workgroup each and at least one chunk per wavefront; the
+// descriptor's schedule field can force either.
 bool use_fused(const msa_decode_desc& d) {
-  const char* env = std::getenv("MSA_DECODE_SCHEDULE");
-  if (env != nullptr && std::strcmp(env, "split") == 0) return false;
-  if (env != nullptr && std::strcmp(env, "fused") == 0) return true;
+  if (d.schedule == MSA_DECODE_SPLIT) return false;
+  if (d.schedule == MSA_DECODE_FUSED) return true;
   return (long long)d.batch * d.heads_kv >= 2LL * device_cus() && d.num_splits >= kFusedWaves;
 }
 

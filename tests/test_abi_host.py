@@ -93,7 +93,7 @@ def test_python_binding_raises():
 
 def dec_desc(**kw):
     args = dict(batch=2, heads_q=8, heads_kv=2, ctx_len=512, head_dim=128, window=64, num_landmarks=8,
-                num_splits=4, scale=0.1, in_dtype=msa.MSA_DTYPE_BF16, out_dtype=msa.MSA_DTYPE_BF16)
+                num_splits=4, scale=0.1, in_dtype=msa.MSA_DTYPE_BF16, out_dtype=msa.MSA_DTYPE_BF16, schedule=0)
     args.update(kw)
     return msa.DecodeDesc(*[args[k] for k, _ in msa.DecodeDesc._fields_])
 
@@ -101,7 +101,8 @@ def dec_desc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(num_splits=0), 1), (dict(window=0), 1), (dict(num_landmarks=7), 1), (dict(ctx_len=0), 1),
     (dict(heads_q=6, heads_kv=4), 1), (dict(heads_q=64, heads_kv=2), 2), (dict(head_dim=32), 2),
-    (dict(in_dtype=msa.MSA_DTYPE_F32), 2), (dict(ctx_len=1 << 23), 2),
+    (dict(in_dtype=msa.MSA_DTYPE_F32), 2), (dict(ctx_len=1 << 23), 2), (dict(schedule=3), 1),
+    (dict(schedule=-1), 1),
 ])
 def test_decode_validation(kw, status):
     d = dec_desc(**kw)

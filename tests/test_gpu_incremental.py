@@ -61,8 +61,7 @@ VARLEN = [
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("B,Hq,Hkv,C,d,w,G,S,lens", VARLEN)
-def test_decode_varlen_small(B, Hq, Hkv, C, d, w, G, S, lens, schedule, monkeypatch):
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+def test_decode_varlen_small(B, Hq, Hkv, C, d, w, G, S, lens, schedule):
     print(f"[case] decode_varlen {schedule} B={B} Hq={Hq} Hkv={Hkv} C={C} d={d} w={w} G={G} S={S} "
           f"lens={lens}", flush=True)
     q = rand((B, Hq, d), 21)
@@ -74,10 +73,10 @@ def test_decode_varlen_small(B, Hq, Hkv, C, d, w, G, S, lens, schedule, monkeypa
     desc = msa.decode_desc(B, Hq, Hkv, C, d, w, G, S, scale, msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_F32)
     ws = torch.empty(msa.msa_decode_workspace_size(desc) // 4, dtype=torch.float32, device=dev())
     O32, L32 = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32,
-                                         workspace=ws)
+                                         workspace=ws, schedule=schedule)
     po, pl = msa.decode_partials(ws, S, B, Hq, d)
     po, pl = host64(po), host64(pl)
-    O16, _ = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale)
+    O16, _ = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, schedule=schedule)
     torch.cuda.synchronize()
     L = C // G if G else 1
     q64, k64, v64 = host64(q), host64(Kc), host64(Vc)
@@ -99,16 +98,15 @@ def test_decode_varlen_small(B, Hq, Hkv, C, d, w, G, S, lens, schedule, monkeypa
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
-def test_decode_varlen_full_lengths_equal_static(schedule, monkeypatch):
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+def test_decode_varlen_full_lengths_equal_static(schedule):
     print(f"[case] decode_varlen {schedule} full lengths vs static", flush=True)
     B, Hq, Hkv, C, d, w, G, S = 4, 8, 2, 4096, 128, 200, 64, 8
     q = rand((B, Hq, d), 31)
     Kc, Vc = rand((B, Hkv, C, d), 32), rand((B, Hkv, C, d), 33)
     Kb, Vb = msa.msa_pool_landmarks(Kc, Vc, G)
     lens_d = torch.full((B,), C, dtype=torch.int32, device=dev())
-    Ov, Lv = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, out_dtype=torch.float32)
-    Os, Ls = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, out_dtype=torch.float32)
+    Ov, Lv = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, out_dtype=torch.float32, schedule=schedule)
+    Os, Ls = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, out_dtype=torch.float32, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(Ov, Os) and torch.equal(Lv, Ls)
 
@@ -132,12 +130,11 @@ def test_decode_varlen_clamps_lengths():
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("d", [128, 64])
-def test_append_then_decode(d, schedule, monkeypatch):
+def test_append_then_decode(d, schedule):
     """Grow four sequences token by token (one idle), decoding after every
     append; each step is graded against the oracle's decode of the same
     prefix, and the landmarks kept by the appends must equal, bit for bit,
     pooling the final cache."""
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
     B, Hq, Hkv, C, w, G, S, steps = 4, 8, 2, 1024, 40, 64, 6, 48
     L = C // G
     print(f"[case] append+decode {schedule} d={d} B={B} C={C} L={L} steps={steps}", flush=True)
@@ -162,7 +159,7 @@ def test_append_then_decode(d, schedule, monkeypatch):
                 v_ref[b, :, pos[b]] = host64(v_new[t, b])
         lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
         O, LSE = msa.msa_decode_fwd_varlen(qs[t], Kc, Vc, Kb, Vb, lens_d, w, G, S, scale,
-                                           out_dtype=torch.float32)
+                                           out_dtype=torch.float32, schedule=schedule)
         torch.cuda.synchronize()
         live = [b for b in range(B) if lens[b] > 0]
         o_ref, l_ref = orc.decode_varlen(host64(qs[t])[live], k_ref[live], v_ref[live],
@@ -207,8 +204,7 @@ def to_pages(Kc, Vc, page, seed, extra=3):
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("page", [32, 64, 256])
-def test_paged_decode_equals_contiguous(page, schedule, monkeypatch):
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+def test_paged_decode_equals_contiguous(page, schedule):
     B, Hq, Hkv, C, d, w, G, S, lens = VARLEN[0]
     print(f"[case] paged decode {schedule} page={page} B={B} C={C} lens={lens}", flush=True)
     q = rand((B, Hq, d), 61)
@@ -218,8 +214,8 @@ def test_paged_decode_equals_contiguous(page, schedule, monkeypatch):
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
     Kp, Vp, table, perm = to_pages(Kc, Vc, page, 64 + page)
     scale = 1.0 / math.sqrt(d)
-    Oc, Lc = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
-    Op, Lp = msa.msa_decode_fwd_paged(q, Kp, Vp, table, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
+    Oc, Lc = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32, schedule=schedule)
+    Op, Lp = msa.msa_decode_fwd_paged(q, Kp, Vp, table, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32, schedule=schedule)
     torch.cuda.synchronize()
     # same rows, same tiles, same order: the same bits
     assert torch.equal(Op, Oc) and torch.equal(Lp, Lc)
@@ -232,10 +228,9 @@ def test_paged_decode_equals_contiguous(page, schedule, monkeypatch):
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
-def test_paged_append_then_decode_equals_contiguous(schedule, monkeypatch):
+def test_paged_append_then_decode_equals_contiguous(schedule):
     """The append + decode sequence of test_append_then_decode on paged caches
     gives the bits of the contiguous run at every step."""
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
     B, Hq, Hkv, C, d, w, G, S, steps, page = 4, 8, 2, 1024, 128, 40, 64, 6, 40, 32
     L = C // G
     print(f"[case] paged append+decode {schedule} page={page} steps={steps}", flush=True)
@@ -255,8 +250,8 @@ def test_paged_append_then_decode_equals_contiguous(schedule, monkeypatch):
         msa.msa_append_kv_paged(k_new[t], v_new[t], pos, Kp, Vp, table, Kbp, Vbp, G)
         lens = [min(C, lens[b] + 1) if not idle[b] else lens[b] for b in range(B)]
         lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
-        Oc, Lc = msa.msa_decode_fwd_varlen(qs[t], Kc, Vc, Kb, Vb, lens_d, w, G, S, out_dtype=torch.float32)
-        Op, Lp = msa.msa_decode_fwd_paged(qs[t], Kp, Vp, table, Kbp, Vbp, lens_d, w, G, S, out_dtype=torch.float32)
+        Oc, Lc = msa.msa_decode_fwd_varlen(qs[t], Kc, Vc, Kb, Vb, lens_d, w, G, S, out_dtype=torch.float32, schedule=schedule)
+        Op, Lp = msa.msa_decode_fwd_paged(qs[t], Kp, Vp, table, Kbp, Vbp, lens_d, w, G, S, out_dtype=torch.float32, schedule=schedule)
         torch.cuda.synchronize()
         assert torch.equal(Op, Oc) and torch.equal(Lp, Lc), t
     assert torch.equal(Kbp, Kb) and torch.equal(Vbp, Vb)
@@ -268,11 +263,10 @@ def test_paged_append_then_decode_equals_contiguous(schedule, monkeypatch):
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
-def test_paged_decode_64k(schedule, monkeypatch):
+def test_paged_decode_64k(schedule):
     """A 64K-token capacity with the full window and 1024-row landmark blocks:
     paged (64-row pages, random permutation) equals contiguous bit for bit,
     and two sequences are graded against the oracle."""
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
     B, Hq, Hkv, C, d, w, G, S, page = 4, 32, 4, 65536, 128, 4096, 64, 16, 64
     print(f"[case] paged decode 64k {schedule}", flush=True)
     lens = [int(x) for x in np.random.default_rng(90).integers(C // 2, C + 1, size=B)]
@@ -283,8 +277,8 @@ def test_paged_decode_64k(schedule, monkeypatch):
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev())
     Kp, Vp, table, perm = to_pages(Kc, Vc, page, 94)
     scale = 1.0 / math.sqrt(d)
-    Oc, Lc = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
-    Op, Lp = msa.msa_decode_fwd_paged(q, Kp, Vp, table, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32)
+    Oc, Lc = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32, schedule=schedule)
+    Op, Lp = msa.msa_decode_fwd_paged(q, Kp, Vp, table, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(Op, Oc) and torch.equal(Lp, Lc)
     for b in (0, 3):

@@ -230,8 +230,7 @@ DEC = [
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("B,Hq,Hkv,ctx,d,w,G,S", DEC)
-def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S, schedule, monkeypatch):
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S, schedule):
     print(f"[case] decode {schedule} B={B} Hq={Hq} Hkv={Hkv} ctx={ctx} d={d} w={w} G={G} S={S}", flush=True)
     q = rand((B, Hq, d), 9, torch.bfloat16)
     Kc = rand((B, Hkv, ctx, d), 10, torch.bfloat16)
@@ -240,10 +239,10 @@ def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S, schedule, monkeypatch):
     Kb, Vb = msa.msa_pool_landmarks(Kc, Vc, G) if G else (None, None)
     desc = msa.decode_desc(B, Hq, Hkv, ctx, d, w, G, S, scale, msa.MSA_DTYPE_BF16, msa.MSA_DTYPE_F32)
     ws = torch.empty(msa.msa_decode_workspace_size(desc) // 4, dtype=torch.float32, device=dev())
-    O32, L32 = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, scale, out_dtype=torch.float32, workspace=ws)
+    O32, L32 = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, scale, out_dtype=torch.float32, workspace=ws, schedule=schedule)
     po, pl = msa.decode_partials(ws, S, B, Hq, d)
     po, pl = host64(po), host64(pl)
-    O16, L16 = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, scale)
+    O16, L16 = msa.msa_decode_fwd(q, Kc, Vc, Kb, Vb, w, G, S, scale, schedule=schedule)
     torch.cuda.synchronize()
     q64, k64, v64 = host64(q), host64(Kc), host64(Vc)
     o_ref, l_ref = orc.decode(q64, k64, v64, w, G, scale)
@@ -270,8 +269,7 @@ def test_decode_small(B, Hq, Hkv, ctx, d, w, G, S, schedule, monkeypatch):
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
-def test_decode_equals_prefill_last_row(schedule, monkeypatch):
-    monkeypatch.setenv("MSA_DECODE_SCHEDULE", schedule)
+def test_decode_equals_prefill_last_row(schedule):
     print(f"[case] decode {schedule} vs prefill row", flush=True)
     B, Hq, Hkv, n, d, w, G = 2, 8, 2, 2048, 128, 200, 16
     Q = rand((B, Hq, n, d), 12, torch.bfloat16)
@@ -281,7 +279,7 @@ def test_decode_equals_prefill_last_row(schedule, monkeypatch):
     O, L = msa.msa_attn_fwd(Q, K, V, Kb, Vb, w, G, out_dtype=torch.float32)
     q = Q[:, :, -1].contiguous()
     for S in (1, 2, 5, 16):
-        Od, Ld = msa.msa_decode_fwd(q, K, V, Kb, Vb, w, G, S, out_dtype=torch.float32)
+        Od, Ld = msa.msa_decode_fwd(q, K, V, Kb, Vb, w, G, S, out_dtype=torch.float32, schedule=schedule)
         torch.cuda.synchronize()
         assert (Od - O[:, :, -1]).abs().max().item() < 2e-3
         assert (Ld - L[:, :, -1]).abs().max().item() < 1e-4
@@ -303,26 +301,17 @@ def dec512k():
     ws = torch.empty(msa.msa_decode_workspace_size(desc) // 4, dtype=torch.float32, device=dev())
     args = (q, Kc, Vc, Kb, Vb, cfg.window, cfg.num_landmarks, cfg.num_splits, cfg.scale)
     r = {"cfg": cfg, "q": q, "Kc": Kc, "Vc": Vc}
-    os.environ.pop("MSA_DECODE_SCHEDULE", None)
     r["O32"], r["L32"] = msa.msa_decode_fwd(*args, out_dtype=torch.float32)
     r["O16"], _ = msa.msa_decode_fwd(*args)
-    os.environ["MSA_DECODE_SCHEDULE"] = "split"
-    try:
-        r["Os"], r["Ls"] = msa.msa_decode_fwd(*args, out_dtype=torch.float32, workspace=ws)
-    finally:
-        os.environ.pop("MSA_DECODE_SCHEDULE", None)
+    r["Os"], r["Ls"] = msa.msa_decode_fwd(*args, out_dtype=torch.float32, workspace=ws, schedule="split")
     po, pl = msa.decode_partials(ws, cfg.num_splits, cfg.batch, cfg.heads_q, cfg.head_dim)
     r["po"], r["pl"] = host64(po[:, 0]), host64(pl[:, 0])
     # the same caches holding sequences of different lengths (incremental decode)
     r["lens"] = wl.decode_lengths(cfg.batch, cfg.ctx_len)
     lens_d = torch.from_numpy(r["lens"]).to(dev())
     r["Ov"], r["Lv"] = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, *args[5:], out_dtype=torch.float32)
-    os.environ["MSA_DECODE_SCHEDULE"] = "split"
-    try:
-        r["Ovs"], r["Lvs"] = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, *args[5:],
-                                                       out_dtype=torch.float32, workspace=ws)
-    finally:
-        os.environ.pop("MSA_DECODE_SCHEDULE", None)
+    r["Ovs"], r["Lvs"] = msa.msa_decode_fwd_varlen(q, Kc, Vc, Kb, Vb, lens_d, *args[5:], out_dtype=torch.float32,
+                                                   workspace=ws, schedule="split")
     torch.cuda.synchronize()
     del Kb, Vb, ws
     yield r
