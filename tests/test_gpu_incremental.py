@@ -219,6 +219,15 @@ def test_paged_decode_equals_contiguous(page, schedule):
     torch.cuda.synchronize()
     # same rows, same tiles, same order: the same bits
     assert torch.equal(Op, Oc) and torch.equal(Lp, Lc)
+    # pages past each sequence's length are never looked up: unmapping them
+    # (id -1) changes nothing
+    cut = table.clone()
+    for b, n in enumerate(lens):
+        cut[b, -(-n // page):] = -1
+    Ou, Lu = msa.msa_decode_fwd_paged(q, Kp, Vp, cut, Kb, Vb, lens_d, w, G, S, scale, out_dtype=torch.float32,
+                                      schedule=schedule)
+    torch.cuda.synchronize()
+    assert torch.equal(Ou, Oc) and torch.equal(Lu, Lc)
     # and against the oracle over the gathered pools
     k64 = orc.gather_pages(host64(Kp), perm, page)
     v64 = orc.gather_pages(host64(Vp), perm, page)
