@@ -380,6 +380,8 @@ def msa_decode_fwd_paged(q, Kpages, Vpages, block_table, Kbar, Vbar, ctx_lens, w
     if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
         raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
     cap = block_table.shape[1] * page
+    if cap >= 1 << 31:
+        raise ValueError(f"capacity {cap} (pages per sequence x page) must be < 2^31 rows")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
     desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
@@ -410,6 +412,8 @@ def msa_append_kv_paged(k_new, v_new, positions, Kpages, Vpages, block_table, Kb
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise ValueError("block_table must be int32 [B][pages per sequence]")
     cap = block_table.shape[1] * page
+    if cap >= 1 << 31:
+        raise ValueError(f"capacity {cap} (pages per sequence x page) must be < 2^31 rows")
     desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kpages.dtype))
     _check(lib().msa_append_kv_paged(ctypes.byref(desc), page, num_pages, _ptr(block_table), _ptr(positions),
                                      _ptr(k_new), _ptr(v_new), _ptr(Kpages), _ptr(Vpages), _ptr(Kbar), _ptr(Vbar),
