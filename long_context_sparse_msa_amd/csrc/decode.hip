@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     const float wl = lc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lc - M) * kLog2e);  // empty chunk: 0
     tot += wl;
     const int nc = min(64, S - c0);
-    constexpr int kU = 8;
+    constexpr int kU = 32;
     for (int cc = 0; cc < nc; cc += kU) {
       float v[kU][kPer];
       float wt[kU];
