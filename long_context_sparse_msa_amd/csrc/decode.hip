@@ -128,22 +128,19 @@ struct Stager {
       const int r = sl / T::CH, p = sl % T::CH;
       const int e = entry(e0, cnt, i);
       const bool is_lm = e < lm;
-      const unsigned char *ks, *vs;
-      if (is_lm) {
-        ks = kl + (size_t)e * T::RB;
-        vs = vl + (size_t)e * T::RB;
-      } else if constexpr (PAGED) {
-        const int row = win0 + e - lm;
+      // both candidate addresses, then a select (no divergent branches)
+      const int row = max(win0 + e - lm, 0);
+      size_t off;
+      if constexpr (PAGED) {
         int id = (row >> shift) == pg.lpA ? pg.idA : pg.idB;
         id = (unsigned)id < (unsigned)num_pages ? id : 0;
-        const size_t off = (size_t)id * pstride + (size_t)(row & ((1 << shift) - 1)) * T::RB;
-        ks = kc + off;
-        vs = vc + off;
+        off = (size_t)id * pstride + (size_t)(row & ((1 << shift) - 1)) * T::RB;
       } else {
-        const size_t row = (size_t)(win0 + e - lm);
-        ks = kc + row * T::RB;
-        vs = vc + row * T::RB;
+        off = (size_t)row * T::RB;
       }
+      const size_t loff = (size_t)e * T::RB;
+      const unsigned char* ks = is_lm ? kl + loff : kc + off;
+      const unsigned char* vs = is_lm ? vl + loff : vc + off;
       __builtin_amdgcn_global_load_lds(ks + (p ^ T::kswz(r)) * 16, (lds_void_ptr)(slot + i * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vs + (p ^ T::vswz(r)) * 16, (lds_void_ptr)(slot + T::BYTES + i * 1024), 16,
                                        0, 0);
