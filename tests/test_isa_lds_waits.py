@@ -42,7 +42,7 @@ def _hipcc():
     return None
 
 
-@pytest.mark.parametrize("src", ["decode.hip", "attn_bf16.hip", "attn_f32.hip", "pool.hip"])
+@pytest.mark.parametrize("src", ["decode.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "pool.hip"])
 def test_kernels_wait_before_use(src, tmp_path):
     hipcc = _hipcc()
     if hipcc is None:
