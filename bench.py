@@ -401,8 +401,8 @@ def measured_peaks(torch, dev, reps=10):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=49152, help="oracle rows per head for the CPU baseline")
     ap.add_argument("--no-1m", action="store_true", help="skip the secondary 1M-token prefill measurement")

@@ -287,31 +287,62 @@ __device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigne
   }
 }
 
-// O = O_acc / sum(bf16 P), LSE = (m + log2 sum(P)) ln 2.
+// O = O_acc / sum(bf16 P), LSE = (m + log2 sum(P)) ln 2.  Called by every
+// thread of the workgroup after the walk's last barrier, when no wavefront
+// reads the tile buffers any more: bf16 rows are staged in LDS (wavefront w
+// owns rows [w*32, w*32+32) of the staging area) and leave it as whole
+// 128-byte lines.  O, LSE and Q are touched once, so they carry the
+// non-temporal hint and leave the L2 to the K/V tiles that the walks of
+// neighbouring query tiles and heads read again.
 template <int D, bool OUT_BF16>
-__device__ __forceinline__ void store_rows(const RowState<D>& st, int row, int n, int g2, size_t q_off,
-                                           size_t lse_off, void* __restrict__ Out, float* __restrict__ LSE) {
+__device__ __forceinline__ void store_rows(const RowState<D>& st, int wr0, int lane, int wave, int n,
+                                           size_t q_off, size_t lse_off, unsigned char* smem,
+                                           void* __restrict__ Out, float* __restrict__ LSE) {
+  const int r32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int row = wr0 + r32;
   const float lt = half_sum(st.l);
   const float lst = half_sum(st.ls);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (row >= n) return;
-  const size_t base = q_off + (size_t)row * D;
+  if constexpr (OUT_BF16) {
+    constexpr int RS = D * 2 + 16;  // staged row stride: 16-byte aligned, rows r and r+16 share banks
+    unsigned char* stage = smem + wave * 32 * RS;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int dcol = db * 32 + jj * 8 + g2 * 4;
-      const float v0 = st.o[db][jj * 4 + 0] * inv, v1 = st.o[db][jj * 4 + 1] * inv;
-      const float v2 = st.o[db][jj * 4 + 2] * inv, v3 = st.o[db][jj * 4 + 3] * inv;
-      if constexpr (OUT_BF16) {
-        const u32x2 pk = {cvt_pk(v0, v1), cvt_pk(v2, v3)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + base + dcol) = pk;
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + base + dcol) = f32x4{v0, v1, v2, v3};
+      for (int jj = 0; jj < 4; ++jj) {
+        const int dcol = db * 32 + jj * 8 + g2 * 4;
+        const u32x2 pk = {cvt_pk(st.o[db][jj * 4 + 0] * inv, st.o[db][jj * 4 + 1] * inv),
+                          cvt_pk(st.o[db][jj * 4 + 2] * inv, st.o[db][jj * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(stage + r32 * RS + dcol * 2) = pk;
+      }
+    }
+    __syncthreads();
+    constexpr int LPR = D * 2 / 16;  // lanes per row, 16 bytes each
+    constexpr int RPI = 64 / LPR;    // rows per store instruction
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int rr = k * RPI + lane / LPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * RS + (lane % LPR) * 16);
+      if (wr0 + rr < n) {
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Out) + q_off + (size_t)(wr0 + rr) * D + (lane % LPR) * 8));
+      }
+    }
+  } else if (row < n) {
+    const size_t base = q_off + (size_t)row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int dcol = db * 32 + jj * 8 + g2 * 4;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + base + dcol) =
+            f32x4{st.o[db][jj * 4 + 0] * inv, st.o[db][jj * 4 + 1] * inv, st.o[db][jj * 4 + 2] * inv,
+                  st.o[db][jj * 4 + 3] * inv};
       }
     }
   }
-  if (LSE != nullptr && g2 == 0) LSE[lse_off + row] = (st.m + log2f(lst)) * kLn2;
+  if (LSE != nullptr && g2 == 0 && row < n) __builtin_nontemporal_store((st.m + log2f(lst)) * kLn2, LSE + lse_off + row);
 }
 
 // Everything a workgroup needs to walk the tiles of one query tile.
@@ -356,7 +387,7 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, size_t q_
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < n) v = *reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row * D + ks * 16 + g2 * 8);
+    if (row < n) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row * D + ks * 16 + g2 * 8));
     qf[ks] = __builtin_bit_cast(bf16x8, v);
   }
 }
@@ -472,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     tile_step<D, 1>(it + 1, smem, sg, wk, fr, qf, st, tc);
   }
   if (it < n_tiles) tile_step<D, 0>(it, smem, sg, wk, fr, qf, st, tc);
-  store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
+  store_rows<D, OUT_BF16>(st, wr0, lane, wave, n, q_off, ((size_t)b * Hq + h) * n, smem, Out, LSE);
 }
 
 // ---------------------------------------------------------------------------
@@ -609,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_list_kernel(
     key_nxt = key_2;
   }
   if (it < wk.count) list_tile_step<D, 0>(key_cur, key_nxt, causal, smem, sg, wk, fr, qf, st, tc);
-  store_rows<D, OUT_BF16>(st, row, n, g2, q_off, ((size_t)b * Hq + h) * n, Out, LSE);
+  store_rows<D, OUT_BF16>(st, wr0, lane, wave, n, q_off, ((size_t)b * Hq + h) * n, smem, Out, LSE);
 }
 
 template <int D, bool OUT_BF16>
