@@ -149,6 +149,7 @@ struct RowState {
   float m;           // running reference max (base-2 units)
   float l;           // this lane's share of sum(bf16 P): normalises O
   float ls;          // this lane's share of sum(P) in float32: gives LSE
+  float thr;         // (m + kRescaleTh) / c2: the raw score above which a tile needs a rescale
 };
 
 // Which keys of a tile a wavefront's rows [wr0, wr1] see: visit the tile at
@@ -190,20 +191,25 @@ __device__ __forceinline__ void mask_tile(f32x16* s, bool is_lm, int key0, int r
 // Online softmax of one tile's scores: raises the reference max when the
 // tile exceeds it by more than 2^kRescaleTh (rescaling O and the sums), then
 // forms P = exp2(s*c2 - m) packed to bf16 as the B operand of O^T += V^T P^T.
+// The common case only compares this lane's largest raw score with the row's
+// bound st.thr (c2 > 0, so s > thr exactly when s*c2 > m + kRescaleTh); the
+// row max over both lanes is formed only when some row needs the rescale.
 // Slots g2*8+0..3 <-> keys kk*16+g2*4+0..3, g2*8+4..7 <-> keys kk*16+8+g2*4+0..3.
 template <int D>
 __device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState<D>& st, bf16x8* pf) {
-  float mx = -INFINITY;
+  float a = fmaxf(s[0][0], s[0][1]);
+  float b = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[mb][e], s[mb][e + 1]));
+  for (int e = 2; e < 16; e += 2) {
+    a = fmaxf(a, fmaxf(s[0][e], s[0][e + 1]));
+    b = fmaxf(b, fmaxf(s[1][e], s[1][e + 1]));
   }
-  mx = half_max(mx) * c2;
-  if (__any(mx > st.m + kRescaleTh)) {
-    const float m_new = fmaxf(st.m, mx);
+  const float lane_max = fmaxf(a, b);
+  if (__any(lane_max > st.thr)) {
+    const float m_new = fmaxf(st.m, half_max(lane_max) * c2);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     st.m = m_new;
+    st.thr = (m_new + kRescaleTh) / c2;
     st.l *= alpha;
     st.ls *= alpha;
 #pragma unroll
@@ -289,11 +295,10 @@ __device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigne
 
 // O = O_acc / sum(bf16 P), LSE = (m + log2 sum(P)) ln 2.  Called by every
 // thread of the workgroup after the walk's last barrier, when no wavefront
-// reads the tile buffers any more: bf16 rows are staged in LDS (wavefront w
-// owns rows [w*32, w*32+32) of the staging area) and leave it as whole
-// 128-byte lines.  O, LSE and Q are touched once, so they carry the
-// non-temporal hint and leave the L2 to the K/V tiles that the walks of
-// neighbouring query tiles and heads read again.
+// reads the tile buffers any more (bf16 rows are staged there).  O, LSE and
+// Q are touched once, so they carry the non-temporal hint and leave the L2
+// to the K/V tiles that the walks of neighbouring query tiles and heads read
+// again.
 template <int D, bool OUT_BF16>
 __device__ __forceinline__ void store_rows(const RowState<D>& st, int wr0, int lane, int wave, int n,
                                            size_t q_off, size_t lse_off, unsigned char* smem,
@@ -305,30 +310,8 @@ __device__ __forceinline__ void store_rows(const RowState<D>& st, int wr0, int l
   const float lst = half_sum(st.ls);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if constexpr (OUT_BF16) {
-    constexpr int RS = D * 2 + 16;  // staged row stride: 16-byte aligned, rows r and r+16 share banks
-    unsigned char* stage = smem + wave * 32 * RS;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int dcol = db * 32 + jj * 8 + g2 * 4;
-        const u32x2 pk = {cvt_pk(st.o[db][jj * 4 + 0] * inv, st.o[db][jj * 4 + 1] * inv),
-                          cvt_pk(st.o[db][jj * 4 + 2] * inv, st.o[db][jj * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(stage + r32 * RS + dcol * 2) = pk;
-      }
-    }
-    __syncthreads();
-    constexpr int LPR = D * 2 / 16;  // lanes per row, 16 bytes each
-    constexpr int RPI = 64 / LPR;    // rows per store instruction
-#pragma unroll
-    for (int k = 0; k < 32 / RPI; ++k) {
-      const int rr = k * RPI + lane / LPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * RS + (lane % LPR) * 16);
-      if (wr0 + rr < n) {
-        __builtin_nontemporal_store(
-            v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Out) + q_off + (size_t)(wr0 + rr) * D + (lane % LPR) * 8));
-      }
-    }
+    store_rows_bf16_nt<D>(st.o, inv, smem + wave * 32 * (D * 2 + 16), lane,
+                          static_cast<uint16_t*>(Out) + q_off + (size_t)wr0 * D, n - wr0);
   } else if (row < n) {
     const size_t base = q_off + (size_t)row * D;
 #pragma unroll
@@ -483,6 +466,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   st.m = -1e30f;
   st.l = 0.f;
   st.ls = 0.f;
+  st.thr = -INFINITY;
 
   Stager<D> sg;
   sg.init(tid);
@@ -613,6 +597,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_list_kernel(
   st.m = -1e30f;
   st.l = 0.f;
   st.ls = 0.f;
+  st.thr = -INFINITY;
 
   Stager<D> sg;
   sg.init(tid);

@@ -280,8 +280,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
     if (row < n) {
-      a = *reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row * D + ks * 16 + g2 * 8);
-      c = *reinterpret_cast<const u32x4*>(dO + q_off + (size_t)row * D + ks * 16 + g2 * 8);
+      a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Q + q_off + (size_t)row * D + ks * 16 + g2 * 8));
+      c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dO + q_off + (size_t)row * D + ks * 16 + g2 * 8));
     }
     qf[ks] = __builtin_bit_cast(bf16x8, a);
     df[ks] = __builtin_bit_cast(bf16x8, c);
@@ -363,19 +363,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     wait_loads_barrier();
   }
 
-  if (row >= n) return;
-  const size_t base = q_off + (size_t)row * D;
+  // dQ is written once: bf16 rows leave through the (now idle) tile buffers
+  // as whole lines, past the L2 that keeps the K/V tiles.
+  if constexpr (OUT_BF16) {
+    store_rows_bf16_nt<D>(dq, scale, smem + wave * 32 * (D * 2 + 16), lane,
+                          static_cast<uint16_t*>(dQ) + q_off + (size_t)wr0 * D, n - wr0);
+  } else if (row < n) {
+    const size_t base = q_off + (size_t)row * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int dcol = db * 32 + jj * 8 + g2 * 4;
-      const float v0 = dq[db][jj * 4 + 0] * scale, v1 = dq[db][jj * 4 + 1] * scale;
-      const float v2 = dq[db][jj * 4 + 2] * scale, v3 = dq[db][jj * 4 + 3] * scale;
-      if constexpr (OUT_BF16) {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dQ) + base + dcol) = u32x2{cvt_pk(v0, v1), cvt_pk(v2, v3)};
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + base + dcol) = f32x4{v0, v1, v2, v3};
+      for (int jj = 0; jj < 4; ++jj) {
+        const int dcol = db * 32 + jj * 8 + g2 * 4;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + base + dcol) =
+            f32x4{dq[db][jj * 4 + 0], dq[db][jj * 4 + 1], dq[db][jj * 4 + 2], dq[db][jj * 4 + 3]} * scale;
       }
     }
   }
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ks * 16 + g2 * 8);
+    if (key < nkeys) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ks * 16 + g2 * 8));
     kf[ks] = __builtin_bit_cast(bf16x8, v);
   }
   const int thr_lane = LM ? (key < A.G ? (key + 1) * A.L - 1 + A.w : 0x7fffffff) : 0;

@@ -46,6 +46,43 @@ __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Stores one wavefront's 32 rows x D of results as bf16.  The values sit in
+// the C layout of 32x32 MFMA accumulators of a transposed product: lane l
+// holds row l%32, dims db*32 + jj*8 + (l/32)*4 + i in acc[db][jj*4+i].  Each
+// is multiplied by `mul` (per lane), staged in `stage` (this wavefront's
+// 32*(2D+16) bytes of LDS) and written so that every store instruction covers
+// whole 128-byte lines, with the non-temporal hint: results written once need
+// no place in the L2.  Rows at or past `nrows` are not written.  Every thread
+// of the workgroup must call it, after the last read of the LDS it reuses.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16_nt(const f32x16* acc, float mul, unsigned char* stage, int lane,
+                                                   uint16_t* dst_row0, int nrows) {
+  constexpr int RS = D * 2 + 16;  // staged row stride: 16-byte aligned, rows r and r+16 share banks
+  const int r32 = lane & 31;
+  const int g2 = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dcol = db * 32 + jj * 8 + g2 * 4;
+      const u32x2 pk = {cvt_pk(acc[db][jj * 4 + 0] * mul, acc[db][jj * 4 + 1] * mul),
+                        cvt_pk(acc[db][jj * 4 + 2] * mul, acc[db][jj * 4 + 3] * mul)};
+      *reinterpret_cast<u32x2*>(stage + r32 * RS + dcol * 2) = pk;
+    }
+  }
+  __syncthreads();
+  constexpr int LPR = D * 2 / 16;  // lanes per row, 16 bytes each
+  constexpr int RPI = 64 / LPR;    // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int rr = k * RPI + lane / LPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * RS + (lane % LPR) * 16);
+    if (rr < nrows) {
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst_row0 + (size_t)rr * D + (lane % LPR) * 8));
+    }
+  }
+}
+
 // (x[l], x[l^32]) for every lane l, as a pair whose max or sum is the
 // value over both halves of the wavefront.
 __device__ __forceinline__ float half_max(float x) {
