@@ -700,10 +700,11 @@ BwdLayout bwd_layout(const msa_attn_desc& d) {
   BwdLayout l;
   const int n = d.seq_len, G = d.num_landmarks;
   l.n_pad = (n + kPad - 1) / kPad * kPad;
-  // segments of query rows for the landmark gradients: at least 4096 rows,
-  // at most 32 segments
-  int seg = (n + 31) / 32;
-  seg = seg < 4096 ? 4096 : seg;
+  // segments of query rows for the landmark gradients: at least 1024 rows,
+  // at most 128 segments (one workgroup per segment and landmark tile: small
+  // enough that the unequal landmark work per segment balances over the CUs)
+  int seg = (n + 127) / 128;
+  seg = seg < 1024 ? 1024 : seg;
   seg = (seg + QB - 1) / QB * QB;
   l.seg = seg;
   l.nseg = G > 0 ? (n + seg - 1) / seg : 0;

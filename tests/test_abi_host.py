@@ -310,7 +310,7 @@ def test_bwd_workspace_size_formula():
         d = base_desc(seq_len=n, num_landmarks=G, heads_q=64, heads_kv=8)
         got = msa.msa_attn_bwd_workspace_size(d)
         n_pad = -(-n // 128) * 128
-        seg = max(4096, -(-n // 32))
+        seg = max(1024, -(-n // 128))
         seg = -(-seg // 32) * 32
         nseg = -(-n // seg) if G else 0
         up = lambda x: -(-x // 256) * 256
