@@ -334,19 +334,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + voff[ks] + mb * 32 * S::RB);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
         }
-        float ds[16];
+        // Edge tiles only (a wavefront-uniform branch): scores this lane's row
+        // does not see become -inf, so P = exp2(-inf) = 0 below.  (A select
+        // around the exponential instead compiles to one divergent branch per
+        // element; the empty volatile asm keeps the compiler from turning this
+        // branch into selects executed on every tile.)
+        if (!interior) {
+          asm volatile("");
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = jj * 4 + i;
-            const int key = key0 + mb * 32 + jj * 8 + g2 * 4 + i;
-            bool vis = true;
-            if (!interior) vis = is_lm ? key < lmc : (unsigned)(row - key) < (unsigned)w;
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, nl2)) : 0.f;
-            ds[e] = p * (dp[e] - Drow);
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + mb * 32 + (e / 4) * 8 + g2 * 4 + e % 4;
+            const bool vis = is_lm ? key < lmc : (unsigned)(row - key) < (unsigned)w;
+            s[e] = vis ? s[e] : -INFINITY;
           }
         }
+        float ds[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, nl2)) * (dp[e] - Drow);
         bf16x8 dsf[2];
         pack_b(ds, dsf);
 #pragma unroll
@@ -553,6 +557,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
         const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + voff[ks]);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dp, 0, 0, 0);
       }
+      // edge blocks only (wavefront-uniform; the empty volatile asm keeps it a
+      // branch): unseen scores become -inf, so P = exp2(-inf) = 0 below
+      // (padding rows past n have lse2 = +inf)
+      if (!interior) {
+        asm volatile("");
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qrow = q0 + (e / 4) * 8 + g2 * 4 + e % 4;
+          const bool vis = LM ? qrow >= thr_lane : (unsigned)(qrow - key) < (unsigned)A.w;
+          s[e] = vis ? s[e] : -INFINITY;
+        }
+      }
       // rows jj*8 + g2*4 + i of the block: (lse2, D) pairs, 32 bytes per jj
       float p[16], ds[16];
 #pragma unroll
@@ -565,12 +581,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = jj * 4 + i;
-          const int qrow = q0 + rb + i;
-          bool vis = true;
-          if (!interior) vis = LM ? qrow >= thr_lane : (unsigned)(qrow - key) < (unsigned)A.w;
-          const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], A.c2, -l2[i])) : 0.f;
-          p[e] = pv;
-          ds[e] = pv * (dp[e] - dd[i]);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], A.c2, -l2[i]));
+          ds[e] = p[e] * (dp[e] - dd[i]);
         }
       }
       bf16x8 pf[2], dsf[2];
