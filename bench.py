@@ -155,6 +155,39 @@ def cpu_baseline(cfg, Q, K, V, rows_per_head, heads):
         "sample": f"{cfg.name}: {len(heads)} query heads x {rows_per_head} seeded rows "
                   f"(+edge rows) of KV head {g}, fp64 numpy, landmark pooling included; "
                   f"{dt:.1f} s for {flops:.3e} useful FLOPs",
+        "tiny_fp32_full": cpu_tiny_full(threads),
+    }
+
+
+def cpu_tiny_full(threads):
+    """The whole fp64 oracle on the tiny fp32 workload (every row of every
+    head), on all BLAS threads and on one."""
+    import msa_inputs as wl
+    from oracle import msa_oracle as orc
+
+    cfg = wl.TINY_FP32
+    q, k, v = (x.astype("float64") for x in wl.host_prefill_inputs(cfg))
+    win, lm = visible_pairs(cfg.seq_len, cfg.window, cfg.num_landmarks)
+    flops = 4.0 * cfg.head_dim * (win + lm) * cfg.heads_q * cfg.batch
+
+    def run():
+        t0 = time.perf_counter()
+        orc.attn(q, k, v, cfg.window, cfg.num_landmarks, cfg.scale)
+        return time.perf_counter() - t0
+
+    t_all = min(run() for _ in range(2))
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t_one = min(run() for _ in range(2))
+    except ImportError:
+        t_one = None
+    return {
+        "seconds": round(t_all, 4), "threads": int(threads),
+        "TFLOP/s": flops / t_all / 1e12,
+        "seconds_1_thread": None if t_one is None else round(t_one, 4),
+        "TFLOP/s_1_thread": None if t_one is None else flops / t_one / 1e12,
+        "flops": flops,
     }
 
 
