@@ -101,23 +101,20 @@ struct Stager {
     const int r = (i * 64 + lane) / T::CH;
     return e0 + (r < cnt ? r : 0);
   }
-  // Page ids of this lane's window rows of the tile at e0 (vector loads).
+  // Page ids of the tile at e0 (cnt >= 1 entries).  Its window rows are one
+  // contiguous run spanning at most two pages (TE <= page), so both ids are
+  // the same for every lane: they are read with uniform indices, which the
+  // compiler turns into scalar loads, so the vector-memory counter that the
+  // loop waits on covers only tile data.
   __device__ __forceinline__ PageIds fetch(int e0, int cnt) const {
-    int lo = 0x7fffffff, hi = 0;
-#pragma unroll
-    for (int i = 0; i < T::KI; ++i) {
-      const int e = entry(e0, cnt, i);
-      if (e >= lm) {
-        const int row = win0 + e - lm;
-        lo = min(lo, row);
-        hi = max(hi, row);
-      }
-    }
-    PageIds pg;
-    pg.lpA = lo == 0x7fffffff ? 0 : lo >> shift;
-    const int lpB = hi >> shift;
-    pg.idA = tbl[min(pg.lpA, max_pages - 1)];
-    pg.idB = tbl[min(lpB, max_pages - 1)];
+    PageIds pg{0, 0, 0};
+    const int ea = max(e0, lm);
+    const int eb = e0 + cnt - 1;
+    if (eb < ea) return pg;  // landmark entries only
+    pg.lpA = __builtin_amdgcn_readfirstlane((win0 + ea - lm) >> shift);
+    const int lpB = __builtin_amdgcn_readfirstlane((win0 + eb - lm) >> shift);
+    pg.idA = tbl[__builtin_amdgcn_readfirstlane(min(pg.lpA, max_pages - 1))];
+    pg.idB = tbl[__builtin_amdgcn_readfirstlane(min(lpB, max_pages - 1))];
     return pg;
   }
   template <bool PAGED>
