@@ -214,6 +214,24 @@ def test_attn_1m_kv_group(gqa1m, g):
                f"{cfg.name} kv{g}", group_span=4096)
 
 
+def test_attn_compression_tokens_128k():
+    """Landmarks at the pages' finer granularity: 256 compression tokens per
+    8K chunk (L = 32, so G = n/32 = 4096 landmarks) at 128K tokens, one KV
+    group of 8 query heads; rows sampled per head."""
+    B, Hq, Hkv, n, d, w, G = 1, 8, 1, 131072, 128, 4096, 4096
+    print(f"[case] compression tokens n={n} w={w} G={G}", flush=True)
+    Q = rand((B, Hq, n, d), 21, torch.bfloat16)
+    K = rand((B, Hkv, n, d), 22, torch.bfloat16)
+    V = rand((B, Hkv, n, d), 23, torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    O32, L32 = run_attn(Q, K, V, w, G, scale, out_dtype=torch.float32)
+    O16, _ = run_attn(Q, K, V, w, G, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(O16, bf16_rne(O32))
+    rows = {h: wl.sample_rows(n, h, 1024, w, n // G) for h in range(Hq)}
+    check_rows(Q, K, V, O32, L32, w, G, scale, rows, TOL_BF16, "compression tokens 128k", group_span=4096)
+
+
 # ------------------------------------------------------------------ decode
 
 DEC = [
@@ -225,6 +243,7 @@ DEC = [
     (2, 2, 2, 1, 128, 1, 1, 2),         # a single cached token
     (1, 8, 8, 4096, 128, 300, 16, 7),
     (2, 6, 2, 2048, 128, 129, 32, 1),   # unsplit
+    (2, 8, 1, 65536, 128, 4096, 2048, 16),  # 32-token landmarks (256 per 8K): 1920 visible
 ]
 
 
