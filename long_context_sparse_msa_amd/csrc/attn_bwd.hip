@@ -14,18 +14,19 @@
 // to the L rows of its block with weight 1/L (a landmark is their mean).
 //
 // Kernels, in launch order:
-//  1. bwd_prep_kernel: D = rowsum(dO * O) and LSE in base 2, per row, into
-//     a padded workspace array (rows past n get LSE = +inf, so P = 0).
-//  2. bwd_dq_kernel: one 128-row query tile of one head per workgroup,
-//     walking the same landmark and window key tiles as the forward.  Per
-//     64-key tile and wavefront (32 rows): S^T = K Q^T and dP^T = V dO^T on
-//     v_mfma_f32_32x32x16_bf16, P and dS in registers (each lane holds 16
-//     keys of one row), dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16.
-//  3. bwd_dkdv_kernel<landmarks>: one workgroup per 128 landmarks and one
+//  1. bwd_dq_kernel: one 128-row query tile of one head per workgroup,
+//     walking the same landmark and window key tiles as the forward.  It
+//     first forms D = rowsum(dO * O) and the base-2 LSE of its rows and
+//     stores them in a padded workspace array for the dK/dV kernels (rows
+//     past n get LSE = +inf, so P = 0).  Per 64-key tile and wavefront (32
+//     rows): S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16, P
+//     and dS in registers (each lane holds 16 keys of one row), dQ^T +=
+//     K^T dS^T with K^T read by ds_read_b64_tr_b16.
+//  2. bwd_dkdv_kernel<landmarks>: one workgroup per 128 landmarks and one
 //     segment of query rows; per-segment partial gradients of the landmarks
 //     go to the workspace.
-//  4. bwd_lm_reduce_kernel: sums the segments (fixed order, deterministic).
-//  5. bwd_dkdv_kernel<window>: one workgroup per 128 keys of one KV head,
+//  3. bwd_lm_reduce_kernel: sums the segments (fixed order, deterministic).
+//  4. bwd_dkdv_kernel<window>: one workgroup per 128 keys of one KV head,
 //     wavefront w owning keys 32w..32w+31, looping over every (query head of
 //     the group, 32-row query block) that sees them.  S = Q K^T and
 //     dP = dO V^T put one key per lane column, so P and dS are directly the
@@ -160,40 +161,7 @@ __device__ __forceinline__ void pack_b(const float* x, bf16x8* out) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D and base-2 LSE per row: LD[bh][r] = (LSE*log2e, rowsum(dO*O)) for
-// r < n, (+inf, 0) for n <= r < n_pad.  16 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE, float2* __restrict__ LD, int n,
-                                                       int n_pad, long long rows_total) {
-  const long long r_glob = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  if (r_glob >= rows_total) return;
-  const long long bh = r_glob / n_pad;
-  const int r = (int)(r_glob - bh * n_pad);
-  float acc = 0.f;
-  if (r < n) {
-    const size_t base = ((size_t)bh * n + r) * D;
-#pragma unroll
-    for (int c = sub; c < D / 8; c += 16) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(O + base + c * 8);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(dO + base + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf16_bits_to_f32(a[e] & 0xffffu), bf16_bits_to_f32(b[e] & 0xffffu), acc);
-        acc = fmaf(bf16_bits_to_f32(a[e] >> 16), bf16_bits_to_f32(b[e] >> 16), acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int sh = 8; sh >= 1; sh >>= 1) acc += __shfl_xor(acc, sh, 16);
-  if (sub == 0) {
-    LD[r_glob] = r < n ? float2{LSE[(size_t)bh * n + r] * kLog2e, acc} : float2{INFINITY, 0.f};
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dQ: the forward's walk, with dP^T = V dO^T and dQ^T += K^T dS^T.
+// 1. dQ: the forward's walk, with dP^T = V dO^T and dQ^T += K^T dS^T.
 template <int D>
 struct DqSmem {
   static constexpr int TILE = BN * Sw<D>::RB;
@@ -228,7 +196,7 @@ template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Kb, const uint16_t* __restrict__ Vb, const uint16_t* __restrict__ dO,
-    const float2* __restrict__ LD, void* __restrict__ dQ, int Hq, int Hkv, int n, int n_pad, int w, int G, int L,
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE, float2* __restrict__ LD, void* __restrict__ dQ, int Hq, int Hkv, int n, int n_pad, int w, int G, int L,
     float c2, float scale, int T) {
   using SM = DqSmem<D>;
   using S = Sw<D>;
@@ -286,8 +254,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     qf[ks] = __builtin_bit_cast(bf16x8, a);
     df[ks] = __builtin_bit_cast(bf16x8, c);
   }
-  const float2 ld = LD[((size_t)b * Hq + h) * n_pad + row];  // row < n_pad always
-  const float nl2 = -ld.x, Drow = ld.y;
+  // D = rowsum(dO * O) over this lane's half of the dims and its partner's
+  // (lane l^32), and the base-2 LSE; both kept for the dK/dV kernels in the
+  // padded array (every row < n_pad belongs to exactly one lane with g2 = 0)
+  float dsum = 0.f;
+  if (row < n) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(O + q_off + (size_t)row * D + ks * 16 + g2 * 8));
+      const u32x4 g = __builtin_bit_cast(u32x4, df[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = fmaf(bf16_bits_to_f32(o[e] & 0xffffu), bf16_bits_to_f32(g[e] & 0xffffu), dsum);
+        dsum = fmaf(bf16_bits_to_f32(o[e] >> 16), bf16_bits_to_f32(g[e] >> 16), dsum);
+      }
+    }
+  }
+  const float Drow = half_sum(dsum);
+  const float lse2 = row < n ? LSE[((size_t)b * Hq + h) * n + row] * kLog2e : INFINITY;
+  if (g2 == 0) LD[((size_t)b * Hq + h) * n_pad + row] = float2{lse2, Drow};  // row < n_pad always
+  const float nl2 = -lse2;
 
   // operand offsets: K rows (both swizzle) and V rows (row swizzle) for
   // S^T = K Q^T and dP^T = V dO^T: row r32 (+32 per key half), chunk ks*2+g2
@@ -673,15 +659,10 @@ hipError_t launch_bwd_t(const msa_attn_desc& d, const BwdLayout& lay, const void
   float* lmg = reinterpret_cast<float*>(wsb + lay.lmg_off);
   const float c2 = d.scale * kLog2e;
 
-  const long long rows = (long long)d.batch * d.heads_q * lay.n_pad;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     u16(O), u16(dO), LSE, LD, n, lay.n_pad, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+  hipError_t e;
   const int T = (n + BM - 1) / BM;
   hipLaunchKernelGGL((bwd_dq_kernel<D, OUT_BF16>), dim3((unsigned)((long long)d.batch * d.heads_q * T)),
-                     dim3(kThreads), 0, stream, u16(Q), u16(K), u16(V), u16(Kb), u16(Vb), u16(dO), LD, dQ,
+                     dim3(kThreads), 0, stream, u16(Q), u16(K), u16(V), u16(Kb), u16(Vb), u16(dO), u16(O), LSE, LD, dQ,
                      d.heads_q, d.heads_kv, n, lay.n_pad, d.window, G, L, c2, d.scale, T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
