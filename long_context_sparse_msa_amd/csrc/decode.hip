@@ -29,6 +29,8 @@
 //  * split (few pairs, where chunks are the parallelism): one wavefront per
 //    (sequence, KV head, chunk) writes its partial; decode_merge_kernel
 //    then merges the chunks of each (sequence, query head).
+#include <atomic>
+
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 #include "msa_plan.hpp"
@@ -600,16 +602,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 }
 
 // Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device (relaxed atomics:
+// concurrent first calls on several threads store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // The fused schedule needs enough (sequence, KV head) pairs to fill the
