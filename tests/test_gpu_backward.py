@@ -109,7 +109,7 @@ def test_bwd_deterministic():
 
 @pytest.fixture(scope="module")
 def bwd32k():
-    """bf16_32k (8/8 heads, n 32768, w 4096, G 512; 8 landmark segments)."""
+    """bf16_32k (8/8 heads, n 32768, w 4096, G 512; 32 landmark segments of 1024 rows)."""
     cfg = wl.BF16_32K
     print(f"[case] {cfg.name} backward (fixture)", flush=True)
     Q, K, V = wl.device_prefill_inputs(cfg, dev())
