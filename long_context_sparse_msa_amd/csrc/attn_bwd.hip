@@ -54,7 +54,7 @@ constexpr int BM = kBM_BF16;  // 128 query rows per dQ workgroup
 constexpr int BN = kBN_BF16;  // 64 keys per dQ tile
 constexpr int KB = 128;       // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int QB = 32;        // query rows per dK/dV step
-constexpr int kPad = 128;     // the padded row count of the prep arrays is a multiple of this
+constexpr int kPad = 128;     // the (LSE, D) array pads each head's rows to a multiple of this
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
