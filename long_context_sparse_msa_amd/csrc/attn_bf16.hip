@@ -83,7 +83,7 @@ struct Stager {
   int wv;
 
   __device__ void init(int gtid) {
-    wv = gtid >> 6;
+    wv = wave_index(gtid);
     const int lane = gtid & 63;
 #pragma unroll
     for (int i = 0; i < kInsts; ++i) {
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int r32 = lane & 31;
   const int g2 = lane >> 5;
 
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_list_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int r32 = lane & 31;
   const int g2 = lane >> 5;
 

@@ -87,7 +87,7 @@ struct TileLoader {
   uint32_t off[NI];
   int wv;
   __device__ void init(int tid, bool both) {
-    wv = tid >> 6;
+    wv = wave_index(tid);
     const int lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int b = rest / Hkv;
   const int h = kvh * grp + h_in;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid);
   const int r32 = lane & 31, g2 = lane >> 5;
   zero_lds(smem, SM::BYTES, tid);
 
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
   constexpr int KS = D / 16, DB = D / 32;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid);
   const int r32 = lane & 31, g2 = lane >> 5;
   const int grp = A.Hq / A.Hkv;
 

@@ -144,6 +144,14 @@ __device__ __forceinline__ void lds_wait(int n, T& x, U& y) {
 }
 #undef MSA_LGKM_SWITCH
 
+// Index of this lane's wavefront within the workgroup, as a value the
+// compiler knows to be uniform: what is derived from it (row ranges, LDS
+// destinations of direct-to-LDS loads, tile-visibility tests) then lives in
+// scalar registers and costs no vector instructions per tile.
+__device__ __forceinline__ int wave_index(int tid) {
+  return __builtin_amdgcn_readfirstlane(tid >> 6);
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
