@@ -197,14 +197,15 @@ __device__ __forceinline__ void mask_tile(f32x16* s, bool is_lm, int key0, int r
 // Slots g2*8+0..3 <-> keys kk*16+g2*4+0..3, g2*8+4..7 <-> keys kk*16+8+g2*4+0..3.
 template <int D>
 __device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState<D>& st, bf16x8* pf) {
-  float a = fmaxf(s[0][0], s[0][1]);
-  float b = fmaxf(s[1][0], s[1][1]);
+  // Two chains of three-input maxima (v_max3_f32): 17 instructions for 32 scores.
+  float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+  float b = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
 #pragma unroll
-  for (int e = 2; e < 16; e += 2) {
-    a = fmaxf(a, fmaxf(s[0][e], s[0][e + 1]));
-    b = fmaxf(b, fmaxf(s[1][e], s[1][e + 1]));
+  for (int e = 3; e < 15; e += 2) {
+    a = fmaxf(fmaxf(a, s[0][e]), s[0][e + 1]);
+    b = fmaxf(fmaxf(b, s[1][e]), s[1][e + 1]);
   }
-  const float lane_max = fmaxf(a, b);
+  const float lane_max = fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]));
   if (__any(lane_max > st.thr)) {
     const float m_new = fmaxf(st.m, half_max(lane_max) * c2);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
@@ -245,7 +246,8 @@ __device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState
 
 // The matrix-core work of one step: optionally O^T += V^T P^T for one tile
 // (PV) and S^T = K Q^T for another (QK), as one unrolled stream of operand
-// fragments read from LDS a fixed window ahead of the MFMA consuming them.
+// fragments read from LDS four fragments ahead of the MFMA consuming them,
+// in exactly this order (a scheduling barrier after every step).
 // Consecutive MFMAs use independent accumulators.
 template <int D, bool PV, bool QK>
 __device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigned char* kt, const Frag<D>& fr,
@@ -256,7 +258,7 @@ __device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigne
   constexpr int NPV = PV ? 4 * DB : 0;  // (kk, db), db fastest
   constexpr int NQK = QK ? 2 * KS : 0;  // (ks, mb), mb fastest
   constexpr int N = NPV + NQK;
-  constexpr int W = 6;                  // fragments in flight
+  constexpr int W = 4;                  // fragments in flight
   u32x4 f[N];
   auto load = [&](int i) -> u32x4 {
     if (i < NPV) {
@@ -290,6 +292,12 @@ __device__ __forceinline__ void mma_phase(const unsigned char* vt, const unsigne
       const int ks = q / 2, mb = q % 2;
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
     }
+    // Keep this order: the compiler would otherwise pull the reads in to just
+    // ahead of their MFMA (exposing the LDS latency at every step) and mix
+    // the softmax's vector work into the PV stream.  Whole phases of one
+    // kind per wavefront interleave better with the other wavefront on the
+    // SIMD (about 2.5% faster on the 128K workload, bit-identical output).
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
