@@ -21,10 +21,11 @@
 //  * Softmax in base 2 with scale*log2(e) folded into one FMA per score,
 //    raw v_exp_f32, packed bf16 converts.  O is normalised by the bf16 dot2
 //    sum of the packed P (exactly the P that multiplies V, so a dominant key
-//    gives O = its value), LSE by a float32 sum of P.  The running max is
-//    raised only when a tile's max exceeds it by more than 2^8 in
-//    probability; until then P stays bounded by 256 and O and the sums are
-//    not rescaled -- exact, since they share the same reference.
+//    gives O = its value), LSE by a float32 sum of P.  The reference max is
+//    raised only when a tile's P, summed over one lane's 32 keys, exceeds
+//    2^8; until then P stays bounded by 256 and O and the sums are not
+//    rescaled -- exact, since they share the same reference.  The common
+//    case thus costs one compare on the float32 sum and never forms a max.
 //  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
 //    destination; no registers, no vector ALU work), row-major with 16-byte
 //    chunks XOR-swizzled by row.  K operands are row-per-lane 16-byte reads;
@@ -48,7 +49,7 @@ namespace {
 constexpr int BM = kBM_BF16;  // 128
 constexpr int BN = kBN_BF16;  // 64
 constexpr int kThreads = 256;
-constexpr float kRescaleTh = 8.0f;  // log2 of the largest unnormalised P
+constexpr float kMaxTileSum = 256.0f;  // bound on one lane's sum of unnormalised P over a tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -149,7 +150,6 @@ struct RowState {
   float m;           // running reference max (base-2 units)
   float l;           // this lane's share of sum(bf16 P): normalises O
   float ls;          // this lane's share of sum(P) in float32: gives LSE
-  float thr;         // (m + kRescaleTh) / c2: the raw score above which a tile needs a rescale
 };
 
 // Which keys of a tile a wavefront's rows [wr0, wr1] see: visit the tile at
@@ -188,54 +188,68 @@ __device__ __forceinline__ void mask_tile(f32x16* s, bool is_lm, int key0, int r
   }
 }
 
-// Online softmax of one tile's scores: raises the reference max when the
-// tile exceeds it by more than 2^kRescaleTh (rescaling O and the sums), then
-// forms P = exp2(s*c2 - m) packed to bf16 as the B operand of O^T += V^T P^T.
-// The common case only compares this lane's largest raw score with the row's
-// bound st.thr (c2 > 0, so s > thr exactly when s*c2 > m + kRescaleTh); the
-// row max over both lanes is formed only when some row needs the rescale.
 // Slots g2*8+0..3 <-> keys kk*16+g2*4+0..3, g2*8+4..7 <-> keys kk*16+8+g2*4+0..3.
-template <int D>
-__device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState<D>& st, bf16x8* pf) {
-  // Two chains of three-input maxima (v_max3_f32): 17 instructions for 32 scores.
-  float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-  float b = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
-#pragma unroll
-  for (int e = 3; e < 15; e += 2) {
-    a = fmaxf(fmaxf(a, s[0][e]), s[0][e + 1]);
-    b = fmaxf(fmaxf(b, s[1][e]), s[1][e + 1]);
-  }
-  const float lane_max = fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]));
-  if (__any(lane_max > st.thr)) {
-    const float m_new = fmaxf(st.m, half_max(lane_max) * c2);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-    st.thr = (m_new + kRescaleTh) / c2;
-    st.l *= alpha;
-    st.ls *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
-  }
-  const float nm = -st.m;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+// exp2(s*c2 + nm) of the tile's 32 scores of this lane, in pack order
+// (p[kk*8 + j]: see the slot map above), and their float32 sum.
+__device__ __forceinline__ float exp_tile(const f32x16* s, float c2, float nm, float* p) {
+  float t[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int mb = kk >> 1;
     const int j0 = (kk & 1) * 2;
-    float p[8];
+    float* q = p + kk * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j0 * 4 + i], c2, nm));
-      p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][(j0 + 1) * 4 + i], c2, nm));
+      q[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j0 * 4 + i], c2, nm));
+      q[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][(j0 + 1) * 4 + i], c2, nm));
     }
-    st.ls += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    // Packed words are kept as separate scalars: feeding the dot2 builtin
-    // with elements of a vector under construction is miscompiled by this
-    // toolchain (every dot2 then reads element 0).
-    const uint32_t w0 = cvt_pk(p[0], p[1]);
-    const uint32_t w1 = cvt_pk(p[2], p[3]);
-    const uint32_t w2 = cvt_pk(p[4], p[5]);
-    const uint32_t w3 = cvt_pk(p[6], p[7]);
+    t[kk] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+  }
+  return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+// Online softmax of one tile's scores: forms P = exp2(s*c2 - m) against the
+// row's reference max m, packed to bf16 as the B operand of O^T += V^T P^T.
+// m is raised only when it has fallen too far behind: when some lane's sum
+// of the tile's P exceeds 2^8 (an overflow to +inf included, as on the first
+// tile, where m starts at -1e30).  That tile is then redone against the row
+// max, with O and the sums rescaled.  Either way every P of a tile, and so
+// its sum, stays at most 2^8, and O and the sums share one reference --
+// exact, whatever m is.  The common case costs one compare on top of the
+// float32 sum that LSE needs anyway; the row max (over both lanes) is formed
+// only when the tile is redone.
+template <int D>
+__device__ __forceinline__ void softmax_tile(const f32x16* s, float c2, RowState<D>& st, bf16x8* pf) {
+  float p[32];
+  float tsum = exp_tile(s, c2, -st.m, p);
+  if (__any(!(tsum <= kMaxTileSum))) {
+    // Two chains of three-input maxima (v_max3_f32): 17 instructions for 32 scores.
+    float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float b = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+    for (int e = 3; e < 15; e += 2) {
+      a = fmaxf(fmaxf(a, s[0][e]), s[0][e + 1]);
+      b = fmaxf(fmaxf(b, s[1][e]), s[1][e + 1]);
+    }
+    const float lane_max = fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]));
+    const float m_new = fmaxf(st.m, half_max(lane_max) * c2);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+    st.ls *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+    tsum = exp_tile(s, c2, -st.m, p);
+  }
+  st.ls += tsum;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float* q = p + kk * 8;
+    const uint32_t w0 = cvt_pk(q[0], q[1]);
+    const uint32_t w1 = cvt_pk(q[2], q[3]);
+    const uint32_t w2 = cvt_pk(q[4], q[5]);
+    const uint32_t w3 = cvt_pk(q[6], q[7]);
     st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, st.l, false);
     st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, st.l, false);
     st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, st.l, false);
@@ -474,7 +488,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   st.m = -1e30f;
   st.l = 0.f;
   st.ls = 0.f;
-  st.thr = -INFINITY;
 
   Stager<D> sg;
   sg.init(tid);
@@ -605,7 +618,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_list_kernel(
   st.m = -1e30f;
   st.l = 0.f;
   st.ls = 0.f;
-  st.thr = -INFINITY;
 
   Stager<D> sg;
   sg.init(tid);
