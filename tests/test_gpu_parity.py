@@ -129,6 +129,37 @@ def test_attn_small_bf16(B, Hq, Hkv, n, d, w, G):
         assert torch.equal(O32, V.float().repeat_interleave(Hq // Hkv, dim=1))
 
 
+@pytest.mark.parametrize("spike", [0.0, 3.0], ids=["rising", "rising+spikes"])
+def test_attn_rising_scores_bf16(spike):
+    """Scores that keep climbing along every row's walk (coordinate 0 of K
+    grows with the position and coordinate 0 of Q is 2), so the running
+    reference max falls behind by more than 2^8 about three times per row
+    after the first tile; with spikes (every 211th key row x3) a single
+    score also overflows exp2 against the old reference on about one tile
+    in ten rows.  The kernel's rescale-and-redo path runs often and must
+    still match the oracle."""
+    print(f"[case] attn bf16 rising scores spike={spike}", flush=True)
+    B, Hq, Hkv, n, d, w, G = 1, 4, 2, 2048, 128, 640, 16
+    Q = rand((B, Hq, n, d), 11, torch.float32)
+    Q[..., 0] = 2.0
+    Q = Q.to(torch.bfloat16)
+    K = rand((B, Hkv, n, d), 12, torch.float32)
+    K[..., 0] += 0.2 * torch.arange(n, dtype=torch.float32, device=K.device)
+    if spike:
+        K[:, :, torch.arange(37, n, 211, device=K.device)] *= spike
+    K = K.to(torch.bfloat16)
+    V = rand((B, Hkv, n, d), 13, torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    O32, L32 = run_attn(Q, K, V, w, G, scale, out_dtype=torch.float32)
+    O16, L16 = run_attn(Q, K, V, w, G, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.attn_dense(host64(Q), host64(K), host64(V), w, G, scale)
+    assert np.ptp(l_ref) > 40.0, "the case should span a wide range of row maxima"
+    assert_close(host64(O32), host64(L32), o_ref, l_ref, TOL_BF16, f"bf16 rising scores spike={spike}")
+    assert torch.equal(O16, bf16_rne(O32)), "bf16 store is not RNE of the float32 epilogue"
+    assert torch.equal(L16, L32)
+
+
 def test_attn_small_fp32_d128():
     print("[case] attn fp32 d=128", flush=True)
     B, Hq, Hkv, n, d, w, G = 1, 4, 2, 333, 128, 70, 9
