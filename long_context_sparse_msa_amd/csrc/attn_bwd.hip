@@ -192,6 +192,85 @@ struct DqWalk {
   }
 };
 
+// Per-wavefront constants of the dQ walk.
+struct DqCtx {
+  int wr0, wr1, wlm_lo, wlm_hi, w, row, lmc, g2;
+  bool live;
+  float c2, nl2, Drow;
+};
+
+// One tile of the dQ walk: issue the next tile's loads into the other
+// buffer, then S^T, dP^T, dS^T and dQ^T += K^T dS^T from buffer BUF.  BUF is
+// a compile-time constant, so every operand read takes its tile offset as an
+// immediate (a runtime buffer index costs one address add per read).
+template <int D, int BUF>
+__device__ __forceinline__ void dq_step(int it, unsigned char* smem, const DqWalk<D>& wk, const DqCtx& c,
+                                        const bf16x8* qf, const bf16x8* df, const uint32_t* koff,
+                                        const uint32_t* voff, const TrOffsets<D>& tro, f32x16* dq) {
+  using SM = DqSmem<D>;
+  using S = Sw<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  const int wr0 = c.wr0, wr1 = c.wr1, wlm_lo = c.wlm_lo, wlm_hi = c.wlm_hi, w = c.w, row = c.row, lmc = c.lmc;
+  const int g2 = c.g2;
+  const bool live = c.live;
+  const float c2 = c.c2, nl2 = c.nl2, Drow = c.Drow;
+  wk.issue(smem, it + 1, BUF ^ 1);
+  const bool is_lm = wk.is_lm(it);
+  const int key0 = wk.key0(it);
+  bool any, interior;
+  if (is_lm) {
+    any = key0 < wlm_hi;
+    interior = key0 + BN <= wlm_lo;
+  } else {
+    any = key0 <= wr1 && key0 + BN - 1 >= wr0 - w + 1;
+    interior = key0 + BN - 1 <= wr0 && key0 >= wr1 - w + 1;
+  }
+  if (live && any) {
+    const unsigned char* kt = smem + SM::kbuf(BUF);
+    const unsigned char* vt = smem + SM::vbuf(BUF);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + mb * 32 * S::RB);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + voff[ks] + mb * 32 * S::RB);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+      }
+      // Edge tiles only (a wavefront-uniform branch): scores this lane's row
+      // does not see become -inf, so P = exp2(-inf) = 0 below.  (A select
+      // around the exponential instead compiles to one divergent branch per
+      // element; the empty volatile asm keeps the compiler from turning this
+      // branch into selects executed on every tile.)
+      if (!interior) {
+        asm volatile("");
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + mb * 32 + (e / 4) * 8 + g2 * 4 + e % 4;
+          const bool vis = is_lm ? key < lmc : (unsigned)(row - key) < (unsigned)w;
+          s[e] = vis ? s[e] : -INFINITY;
+        }
+      }
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, nl2)) * (dp[e] - Drow);
+      bf16x8 dsf[2];
+      pack_b(ds, dsf);
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        const int rows0 = (mb * 2 + kl) * 16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = tr_pair(kt + rows0 * S::RB, tro.lo[db], tro.hi[db]);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kl], dq[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_loads_barrier();
+}
+
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -294,64 +373,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   wk.issue(smem, 0, 0);
   wait_loads_barrier();
 
-  for (int it = 0; it < wk.n_tiles; ++it) {
-    const int buf = it & 1;
-    wk.issue(smem, it + 1, buf ^ 1);
-    const bool is_lm = wk.is_lm(it);
-    const int key0 = wk.key0(it);
-    bool any, interior;
-    if (is_lm) {
-      any = key0 < wlm_hi;
-      interior = key0 + BN <= wlm_lo;
-    } else {
-      any = key0 <= wr1 && key0 + BN - 1 >= wr0 - w + 1;
-      interior = key0 + BN - 1 <= wr0 && key0 >= wr1 - w + 1;
-    }
-    if (live && any) {
-      const unsigned char* kt = smem + SM::kbuf(buf);
-      const unsigned char* vt = smem + SM::vbuf(buf);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + mb * 32 * S::RB);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + voff[ks] + mb * 32 * S::RB);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
-        }
-        // Edge tiles only (a wavefront-uniform branch): scores this lane's row
-        // does not see become -inf, so P = exp2(-inf) = 0 below.  (A select
-        // around the exponential instead compiles to one divergent branch per
-        // element; the empty volatile asm keeps the compiler from turning this
-        // branch into selects executed on every tile.)
-        if (!interior) {
-          asm volatile("");
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = key0 + mb * 32 + (e / 4) * 8 + g2 * 4 + e % 4;
-            const bool vis = is_lm ? key < lmc : (unsigned)(row - key) < (unsigned)w;
-            s[e] = vis ? s[e] : -INFINITY;
-          }
-        }
-        float ds[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, nl2)) * (dp[e] - Drow);
-        bf16x8 dsf[2];
-        pack_b(ds, dsf);
-#pragma unroll
-        for (int kl = 0; kl < 2; ++kl) {
-          const int rows0 = (mb * 2 + kl) * 16;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 a = tr_pair(kt + rows0 * S::RB, tro.lo[db], tro.hi[db]);
-            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kl], dq[db], 0, 0, 0);
-          }
-        }
-      }
-    }
-    wait_loads_barrier();
+  const DqCtx ctx{wr0, wr1, wlm_lo, wlm_hi, w, row, lmc, g2, live, c2, nl2, Drow};
+  int it = 0;
+  for (; it + 1 < wk.n_tiles; it += 2) {
+    dq_step<D, 0>(it, smem, wk, ctx, qf, df, koff, voff, tro, dq);
+    dq_step<D, 1>(it + 1, smem, wk, ctx, qf, df, koff, voff, tro, dq);
   }
+  if (it < wk.n_tiles) dq_step<D, 0>(it, smem, wk, ctx, qf, df, koff, voff, tro, dq);
 
   // dQ is written once: bf16 rows leave through the (now idle) tile buffers
   // as whole lines, past the L2 that keeps the K/V tiles.
@@ -425,6 +453,88 @@ struct KvStager {
     }
   }
 };
+
+// One query block of the dK/dV walk: issue the next block's loads into the
+// other buffer, then S, dP, dS and dV^T += dO^T P, dK^T += Q^T dS from buffer
+// BUF (a compile-time constant, so every operand read takes its offset as an
+// immediate).
+template <int D, bool LM, int BUF>
+__device__ __forceinline__ void kv_step(int it, const KvArgs& A, const KvStager<D>& st, unsigned char* smem,
+                                        int k0, int key, int thr_lane, int g2, const bf16x8* kf,
+                                        const uint32_t* qoff, const uint32_t* voff, const TrOffsets<D>& tro,
+                                        f32x16* dk, f32x16* dv) {
+  using SM = KvSmem<D>;
+  using S = Sw<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  st.issue(A, smem, it + 1, BUF ^ 1);
+  const int q0 = (st.qb_lo + it % st.nqb) * QB;
+  bool any, interior;
+  if constexpr (LM) {
+    const int thr_lo = (k0 + 1) * A.L - 1 + A.w;
+    const int thr_hi = (k0 + 32) * A.L - 1 + A.w;
+    any = k0 < A.G && q0 + QB - 1 >= thr_lo;
+    interior = k0 + 31 < A.G && q0 >= thr_hi;
+  } else {
+    any = q0 + QB - 1 >= k0 && q0 <= k0 + 31 + A.w - 1;
+    interior = q0 >= k0 + 31 && q0 + QB - 1 <= k0 + A.w - 1;
+  }
+  if (any) {
+    const unsigned char* qt = smem + SM::qbuf(BUF);
+    const unsigned char* ot = smem + SM::obuf(BUF);
+    const float* ldt = reinterpret_cast<const float*>(smem + SM::ldbuf(BUF));
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + qoff[ks]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ot + qoff[ks]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + voff[ks]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dp, 0, 0, 0);
+    }
+    // edge blocks only (wavefront-uniform; the empty volatile asm keeps it a
+    // branch): unseen scores become -inf, so P = exp2(-inf) = 0 below
+    // (padding rows past n have lse2 = +inf)
+    if (!interior) {
+      asm volatile("");
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qrow = q0 + (e / 4) * 8 + g2 * 4 + e % 4;
+        const bool vis = LM ? qrow >= thr_lane : (unsigned)(qrow - key) < (unsigned)A.w;
+        s[e] = vis ? s[e] : -INFINITY;
+      }
+    }
+    // rows jj*8 + g2*4 + i of the block: (lse2, D) pairs, 32 bytes per jj
+    float p[16], ds[16];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int rb = jj * 8 + g2 * 4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ldt + rb * 2);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(ldt + rb * 2 + 4);
+      const float l2[4] = {a[0], a[2], c[0], c[2]};
+      const float dd[4] = {a[1], a[3], c[1], c[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = jj * 4 + i;
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], A.c2, -l2[i]));
+        ds[e] = p[e] * (dp[e] - dd[i]);
+      }
+    }
+    bf16x8 pf[2], dsf[2];
+    pack_b(p, pf);
+    pack_b(ds, dsf);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 oa = tr_pair(ot + kk * 16 * S::RB, tro.lo[db], tro.hi[db]);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[kk], dv[db], 0, 0, 0);
+        const bf16x8 qa = tr_pair(qt + kk * 16 * S::RB, tro.lo[db], tro.hi[db]);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[kk], dk[db], 0, 0, 0);
+      }
+    }
+  }
+  wait_loads_barrier();
+}
 
 template <int D, bool LM, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
@@ -516,77 +626,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs A) {
     dv[db] = f32x16{};
   }
 
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    st.issue(A, smem, it + 1, buf ^ 1);
-    const int q0 = (qb_lo + it % nqb) * QB;
-    bool any, interior;
-    if constexpr (LM) {
-      const int thr_lo = (k0 + 1) * A.L - 1 + A.w;
-      const int thr_hi = (k0 + 32) * A.L - 1 + A.w;
-      any = k0 < A.G && q0 + QB - 1 >= thr_lo;
-      interior = k0 + 31 < A.G && q0 >= thr_hi;
-    } else {
-      any = q0 + QB - 1 >= k0 && q0 <= k0 + 31 + A.w - 1;
-      interior = q0 >= k0 + 31 && q0 + QB - 1 <= k0 + A.w - 1;
-    }
-    if (any) {
-      const unsigned char* qt = smem + SM::qbuf(buf);
-      const unsigned char* ot = smem + SM::obuf(buf);
-      const float* ldt = reinterpret_cast<const float*>(smem + SM::ldbuf(buf));
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + qoff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ot + qoff[ks]);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + voff[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dp, 0, 0, 0);
-      }
-      // edge blocks only (wavefront-uniform; the empty volatile asm keeps it a
-      // branch): unseen scores become -inf, so P = exp2(-inf) = 0 below
-      // (padding rows past n have lse2 = +inf)
-      if (!interior) {
-        asm volatile("");
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qrow = q0 + (e / 4) * 8 + g2 * 4 + e % 4;
-          const bool vis = LM ? qrow >= thr_lane : (unsigned)(qrow - key) < (unsigned)A.w;
-          s[e] = vis ? s[e] : -INFINITY;
-        }
-      }
-      // rows jj*8 + g2*4 + i of the block: (lse2, D) pairs, 32 bytes per jj
-      float p[16], ds[16];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rb = jj * 8 + g2 * 4;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(ldt + rb * 2);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(ldt + rb * 2 + 4);
-        const float l2[4] = {a[0], a[2], c[0], c[2]};
-        const float dd[4] = {a[1], a[3], c[1], c[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = jj * 4 + i;
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], A.c2, -l2[i]));
-          ds[e] = p[e] * (dp[e] - dd[i]);
-        }
-      }
-      bf16x8 pf[2], dsf[2];
-      pack_b(p, pf);
-      pack_b(ds, dsf);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 oa = tr_pair(ot + kk * 16 * S::RB, tro.lo[db], tro.hi[db]);
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[kk], dv[db], 0, 0, 0);
-          const bf16x8 qa = tr_pair(qt + kk * 16 * S::RB, tro.lo[db], tro.hi[db]);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[kk], dk[db], 0, 0, 0);
-        }
-      }
-    }
-    wait_loads_barrier();
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
+    kv_step<D, LM, 0>(it, A, st, smem, k0, key, thr_lane, g2, kf, qoff, voff, tro, dk, dv);
+    kv_step<D, LM, 1>(it + 1, A, st, smem, k0, key, thr_lane, g2, kf, qoff, voff, tro, dk, dv);
   }
+  if (it < n_it) kv_step<D, LM, 0>(it, A, st, smem, k0, key, thr_lane, g2, kf, qoff, voff, tro, dk, dv);
 
   // lane (r32, g2) holds dims db*32 + jj*8 + g2*4 + i of key `key`
   if constexpr (LM) {
