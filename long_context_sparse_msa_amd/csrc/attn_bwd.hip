@@ -495,11 +495,15 @@ __device__ __forceinline__ void kv_step(int it, const KvArgs& A, const KvStager<
     // branch): unseen scores become -inf, so P = exp2(-inf) = 0 below
     // (padding rows past n have lse2 = +inf)
     if (!interior) {
-      asm volatile("");
+      // rel = the lane's first row minus its key (minus the landmark's first
+      // seeing row), made opaque so that the per-element row offsets stay
+      // immediates instead of 16 loop-invariant registers
+      int rel = q0 + g2 * 4 - (LM ? thr_lane : key);
+      asm volatile("" : "+v"(rel));
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int qrow = q0 + (e / 4) * 8 + g2 * 4 + e % 4;
-        const bool vis = LM ? qrow >= thr_lane : (unsigned)(qrow - key) < (unsigned)A.w;
+        const int d = rel + (e / 4) * 8 + e % 4;  // qrow - key (qrow - thr_lane)
+        const bool vis = LM ? d >= 0 : (unsigned)d < (unsigned)A.w;
         s[e] = vis ? s[e] : -INFINITY;
       }
     }

@@ -13,10 +13,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "long_context_sparse_msa_amd", "csrc")
 
-# kernels that must not spill at all (the dK/dV kernels park three loop
-# invariants in scratch before their loop and reload them after it)
-NO_SPILL = ("attn_fwd_bf16_kernel", "attn_fwd_list_kernel", "bwd_dq_kernel", "decode_fused_kernel",
-            "decode_split_kernel", "decode_merge_kernel", "pool_kernel", "append_kernel")
+# kernels that must not spill at all
+NO_SPILL = ("attn_fwd_bf16_kernel", "attn_fwd_list_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel",
+            "decode_fused_kernel", "decode_split_kernel", "decode_merge_kernel", "pool_kernel", "append_kernel")
 
 
 def kernel_registers(text: str) -> dict:
