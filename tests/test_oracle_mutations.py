@@ -8,6 +8,7 @@ from tests import test_oracle_backward as bwd
 from tests import test_oracle_blocksparse as bsp
 from tests import test_oracle_incremental as inc
 from tests import test_oracle_pins as pins
+from tests import test_oracle_plan_pins as plan
 
 
 def _window_wide(i, j, w):          # w+1 keys
@@ -104,6 +105,45 @@ def _bs_mask_block_short(n, counts, indices, bq, bk, causal):      # drops each 
     return M
 
 
+def _tile_plan_variant(interior_any=False, k_hi_short=False):
+    """The oracle's tile enumeration with one planted mistake."""
+    def tile_plan(n, w, G, BM, BN, q_tiles=None):
+        T = -(-n // BM)
+        ts = range(T) if q_tiles is None else q_tiles
+        L = orc.block_len(n, G) if G else 0
+        out = []
+        for t in ts:
+            rws = np.arange(t * BM, min(n, t * BM + BM))
+            if G:
+                for lt in range(-(-G // BN)):
+                    b = np.arange(lt * BN, lt * BN + BN)
+                    M = orc.landmark_visible(rws[:, None], b[None, :], L, w) & (b[None, :] < G)
+                    if M.any():
+                        out.append((t, 0, lt, bool(M.any() if interior_any else M.all())))
+            k_lo = max(0, int(rws[0]) - w) // BN
+            k_hi = min(-(-n // BN) - 1, (int(rws[-1]) + 1) // BN)
+            if k_hi_short:
+                k_hi = (int(rws[-1])) // BN - 1
+            for kt in range(k_lo, k_hi + 1):
+                j = np.arange(kt * BN, kt * BN + BN)
+                M = orc.window_visible(rws[:, None], j[None, :], w) & (j[None, :] < n)
+                if M.any():
+                    out.append((t, 1, kt, bool(M.any() if interior_any else M.all())))
+        return out
+    return tile_plan
+
+
+def _row_plan_lo_from_top(n, w, G, rows=None):     # lowest visible key read from the wrong end
+    lo, cnt = orc.__dict__["_orig_row_plan"](n, w, G, rows)
+    r = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    return np.where(r - lo + 1 > 1, r, lo), cnt
+
+
+def _chunk_bounds_floor(E, S):                     # floor(E/S) entries per chunk
+    s = E // S
+    return np.array([min(E, c * s) for c in range(S)] + [E], dtype=np.int64)
+
+
 MUTANTS = {
     "window_wide": ("window_visible", _window_wide),
     "window_no_self": ("window_visible", _window_no_self),
@@ -122,6 +162,10 @@ MUTANTS = {
     "bwd_mean_last_row": ("_mean_bwd", _mean_bwd_last_row),
     "bs_strict_causal": ("blocksparse_mask", _bs_mask_strict_causal),
     "bs_block_short": ("blocksparse_mask", _bs_mask_block_short),
+    "tile_interior_any": ("tile_plan", _tile_plan_variant(interior_any=True)),
+    "tile_k_hi_short": ("tile_plan", _tile_plan_variant(k_hi_short=True)),
+    "row_plan_lo_from_top": ("row_plan", _row_plan_lo_from_top),
+    "chunk_bounds_floor": ("chunk_bounds", _chunk_bounds_floor),
 }
 
 PIN_SET = [
@@ -144,6 +188,10 @@ PIN_SET = [
     lambda: bwd.test_one_token_landmarks_give_causal_backward(7),
     lambda: bsp.test_full_causal_lists_are_causal_sdpa(),
     lambda: bsp.test_brute_force_random_lists(True),
+    lambda: plan.test_tile_plan_equals_brute_force(130, 65, 10, 64, 64),
+    lambda: plan.test_row_plan_equals_brute_force(300, 63, 10),
+    lambda: plan.test_chunk_bounds_decode_workload(),
+    lambda: plan.test_chunk_bounds_with_empty_chunks(),
 ]
 
 
@@ -170,5 +218,6 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(orc.__dict__, "_orig_vlf", orc.visible_list_fixed)
     monkeypatch.setitem(orc.__dict__, "_orig_pool_prefix", orc.pool_prefix)
     monkeypatch.setitem(orc.__dict__, "_orig_bs_mask", orc.blocksparse_mask)
+    monkeypatch.setitem(orc.__dict__, "_orig_row_plan", orc.row_plan)
     monkeypatch.setattr(orc, attr, fn)
     assert _failures() > 0, f"no pin caught the planted mistake {name}"
