@@ -147,6 +147,46 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape=None, dtype=None, optional: bool = False) -> None:
+    """Raise ValueError unless t has this shape and dtype and is contiguous."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(device, **tensors) -> None:
+    """Raise ValueError unless every given tensor lives in GPU memory on
+    `device`.  The library receives raw pointers: a tensor of the wrong size,
+    type or device would otherwise become out-of-bounds device accesses."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be in GPU memory (it is on {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+
+
+def _expect_workspace(ws, need: int) -> None:
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+
+
+def _expect_landmarks(Kbar, Vbar, B, Hkv, G, d, dtype) -> None:
+    """Pooled landmarks [B][Hkv][G][d] in the input dtype (may be None when G = 0)."""
+    _expect(Kbar, "Kbar", (B, Hkv, G, d), dtype, optional=G == 0)
+    _expect(Vbar, "Vbar", (B, Hkv, G, d), dtype, optional=G == 0)
+
+
 def _stream(t, stream) -> Optional[int]:
     import torch
     if stream is not None:
@@ -183,11 +223,15 @@ def msa_pool_landmarks(K, V, num_landmarks: int, Kbar=None, Vbar=None, stream=No
     if V.shape != K.shape or V.dtype != K.dtype:
         raise ValueError("K and V must have the same shape and dtype")
     G = num_landmarks
+    _expect(K, "K")
+    _expect(V, "V")
     if Kbar is None:
         Kbar = torch.empty((B, Hkv, G, d), dtype=K.dtype, device=K.device)
     if Vbar is None:
         Vbar = torch.empty((B, Hkv, G, d), dtype=K.dtype, device=K.device)
+    _expect_landmarks(Kbar, Vbar, B, Hkv, G, d, K.dtype)
     desc = attn_desc(B, Hkv, Hkv, n, d, 1, G, 1.0, _dtype_code(K.dtype))
+    _on_gpu(K.device, K=K, V=V, Kbar=Kbar, Vbar=Vbar)
     _check(lib().msa_pool_landmarks(ctypes.byref(desc), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
                                     _stream(K, stream)))
     return Kbar, Vbar
@@ -205,11 +249,19 @@ def msa_attn_fwd(Q, K, V, Kbar, Vbar, window: int, num_landmarks: int, scale: Op
         raise ValueError("Q, K, V must share a dtype")
     in_code = _dtype_code(Q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    dev = Q.device
+    _expect(Q, "Q")
+    _expect(K, "K")
+    _expect(V, "V")
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, Q.dtype)
     if O is None:
         O = torch.empty((B, Hq, n, d), dtype=_torch_dtype(out_code), device=Q.device)
     if LSE is None and want_lse:
         LSE = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device)
+    _expect(O, "O", (B, Hq, n, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq, n), torch.float32, optional=True)
     desc = attn_desc(B, Hq, Hkv, n, d, window, num_landmarks, scale, in_code, out_code)
+    _on_gpu(dev, Q=Q, K=K, V=V, Kbar=Kbar, Vbar=Vbar, O=O, LSE=LSE)
     _check(lib().msa_attn_fwd(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
                               _ptr(O), _ptr(LSE), _stream(Q, stream)))
     return O, LSE
@@ -231,13 +283,24 @@ def msa_attn_fwd_blocksparse(Q, K, V, block_counts, block_indices, causal: bool,
     if block_indices.dtype != torch.int32 or block_indices.dim() != 4 or \
             tuple(block_indices.shape[:3]) != (B, Hq, T):
         raise ValueError(f"block_indices must be int32 [{B}][{Hq}][{T}][max_blocks]")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K, V must share a dtype")
     in_code = _dtype_code(Q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    dev = Q.device
+    _expect(Q, "Q")
+    _expect(K, "K")
+    _expect(V, "V")
+    _expect(block_counts, "block_counts")
+    _expect(block_indices, "block_indices")
     if O is None:
         O = torch.empty((B, Hq, n, d), dtype=_torch_dtype(out_code), device=Q.device)
     if LSE is None and want_lse:
         LSE = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device)
+    _expect(O, "O", (B, Hq, n, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq, n), torch.float32, optional=True)
     desc = attn_desc(B, Hq, Hkv, n, d, 1, 0, scale, in_code, out_code)
+    _on_gpu(dev, Q=Q, K=K, V=V, block_counts=block_counts, block_indices=block_indices, O=O, LSE=LSE)
     _check(lib().msa_attn_fwd_blocksparse(ctypes.byref(desc), _ptr(block_counts), _ptr(block_indices),
                                           int(block_indices.shape[3]), 1 if causal else 0, _ptr(Q), _ptr(K),
                                           _ptr(V), _ptr(O), _ptr(LSE), _stream(Q, stream)))
@@ -264,12 +327,19 @@ def msa_attn_bwd(Q, K, V, Kbar, Vbar, O, LSE, dO, window: int, num_landmarks: in
         raise ValueError("LSE must be float32 [B][Hq][n]")
     if O.dtype != torch.bfloat16 or dO.dtype != torch.bfloat16:
         raise ValueError("O and dO must be bf16")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K, V must share a dtype")
     in_code = _dtype_code(Q.dtype)
     out_code = MSA_DTYPE_F32 if out_dtype is None else _dtype_code(out_dtype)
+    dev = Q.device
+    for t, name in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (LSE, "LSE"), (dO, "dO")):
+        _expect(t, name)
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, Q.dtype)
     desc = attn_desc(B, Hq, Hkv, n, d, window, num_landmarks, scale, in_code, out_code)
     need = msa_attn_bwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    _expect_workspace(workspace, need)
     ws_bytes = workspace.numel() * workspace.element_size()
     odt = _torch_dtype(out_code)
     if dQ is None:
@@ -278,6 +348,11 @@ def msa_attn_bwd(Q, K, V, Kbar, Vbar, O, LSE, dO, window: int, num_landmarks: in
         dK = torch.empty((B, Hkv, n, d), dtype=odt, device=Q.device)
     if dV is None:
         dV = torch.empty((B, Hkv, n, d), dtype=odt, device=Q.device)
+    _expect(dQ, "dQ", (B, Hq, n, d), odt)
+    _expect(dK, "dK", (B, Hkv, n, d), odt)
+    _expect(dV, "dV", (B, Hkv, n, d), odt)
+    _on_gpu(dev, Q=Q, K=K, V=V, Kbar=Kbar, Vbar=Vbar, O=O, LSE=LSE, dO=dO, workspace=workspace, dQ=dQ, dK=dK,
+            dV=dV)
     _check(lib().msa_attn_bwd(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar), _ptr(O),
                               _ptr(LSE), _ptr(dO), _ptr(workspace), ws_bytes, _ptr(dQ), _ptr(dK), _ptr(dV),
                               _stream(Q, stream)))
@@ -301,17 +376,28 @@ def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_s
     Hkv, ctx = Kc.shape[1], Kc.shape[2]
     if Kc.shape != (B, Hkv, ctx, d) or Vc.shape != Kc.shape:
         raise ValueError("cache shapes do not match q")
+    if Kc.dtype != q.dtype or Vc.dtype != q.dtype:
+        raise ValueError("q and the caches must share a dtype")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    dev = q.device
+    _expect(q, "q")
+    _expect(Kc, "Kc")
+    _expect(Vc, "Vc")
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, q.dtype)
     desc = decode_desc(B, Hq, Hkv, ctx, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
-        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _expect_workspace(workspace, need)
     ws_bytes = workspace.numel() * workspace.element_size()
     if O is None:
         O = torch.empty((B, Hq, d), dtype=_torch_dtype(out_code), device=q.device)
     if LSE is None and want_lse:
         LSE = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _expect(O, "O", (B, Hq, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq), torch.float32, optional=True)
+    _on_gpu(dev, q=q, Kc=Kc, Vc=Vc, Kbar=Kbar, Vbar=Vbar, workspace=workspace, O=O, LSE=LSE)
     _check(lib().msa_decode_fwd(ctypes.byref(desc), _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(Kbar), _ptr(Vbar),
                                 _ptr(workspace), ws_bytes, _ptr(O), _ptr(LSE), _stream(q, stream)))
     return O, LSE
@@ -331,17 +417,29 @@ def msa_decode_fwd_varlen(q, Kc, Vc, Kbar, Vbar, ctx_lens, window: int, num_land
         raise ValueError("cache shapes do not match q")
     if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
         raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
+    if Kc.dtype != q.dtype or Vc.dtype != q.dtype:
+        raise ValueError("q and the caches must share a dtype")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    dev = q.device
+    _expect(q, "q")
+    _expect(Kc, "Kc")
+    _expect(Vc, "Vc")
+    _expect(ctx_lens, "ctx_lens")
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, q.dtype)
     desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
-        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _expect_workspace(workspace, need)
     ws_bytes = workspace.numel() * workspace.element_size()
     if O is None:
         O = torch.empty((B, Hq, d), dtype=_torch_dtype(out_code), device=q.device)
     if LSE is None and want_lse:
         LSE = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _expect(O, "O", (B, Hq, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq), torch.float32, optional=True)
+    _on_gpu(dev, q=q, Kc=Kc, Vc=Vc, ctx_lens=ctx_lens, Kbar=Kbar, Vbar=Vbar, workspace=workspace, O=O, LSE=LSE)
     _check(lib().msa_decode_fwd_varlen(ctypes.byref(desc), _ptr(ctx_lens), _ptr(q), _ptr(Kc), _ptr(Vc),
                                        _ptr(Kbar), _ptr(Vbar), _ptr(workspace), ws_bytes, _ptr(O), _ptr(LSE),
                                        _stream(q, stream)))
@@ -360,7 +458,13 @@ def msa_append_kv(k_new, v_new, positions, Kc, Vc, Kbar, Vbar, num_landmarks: in
         raise ValueError("positions must be an int32 tensor of shape [B]")
     if k_new.dtype != Kc.dtype or v_new.dtype != Kc.dtype or Vc.dtype != Kc.dtype:
         raise ValueError("new rows and caches must share a dtype")
+    dev = Kc.device
+    _expect(Kc, "Kc")
+    for t, name in ((Vc, "Vc"), (k_new, "k_new"), (v_new, "v_new"), (positions, "positions")):
+        _expect(t, name)
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, Kc.dtype)
     desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kc.dtype))
+    _on_gpu(dev, Kc=Kc, Vc=Vc, k_new=k_new, v_new=v_new, positions=positions, Kbar=Kbar, Vbar=Vbar)
     _check(lib().msa_append_kv(ctypes.byref(desc), _ptr(positions), _ptr(k_new), _ptr(v_new), _ptr(Kc),
                                _ptr(Vc), _ptr(Kbar), _ptr(Vbar), _stream(Kc, stream)))
 
@@ -382,17 +486,29 @@ def msa_decode_fwd_paged(q, Kpages, Vpages, block_table, Kbar, Vbar, ctx_lens, w
     cap = block_table.shape[1] * page
     if cap >= 1 << 31:
         raise ValueError(f"capacity {cap} (pages per sequence x page) must be < 2^31 rows")
+    if Kpages.dtype != q.dtype or Vpages.dtype != q.dtype:
+        raise ValueError("q and the page pools must share a dtype")
     in_code = _dtype_code(q.dtype)
     out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    dev = q.device
+    _expect(q, "q")
+    for t, name in ((Kpages, "Kpages"), (Vpages, "Vpages"), (block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        _expect(t, name)
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, q.dtype)
     desc = decode_desc(B, Hq, Hkv, cap, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
     need = msa_decode_workspace_size(desc)
     if workspace is None:
-        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _expect_workspace(workspace, need)
     ws_bytes = workspace.numel() * workspace.element_size()
     if O is None:
         O = torch.empty((B, Hq, d), dtype=_torch_dtype(out_code), device=q.device)
     if LSE is None and want_lse:
         LSE = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _expect(O, "O", (B, Hq, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq), torch.float32, optional=True)
+    _on_gpu(dev, q=q, Kpages=Kpages, Vpages=Vpages, block_table=block_table, ctx_lens=ctx_lens, Kbar=Kbar,
+            Vbar=Vbar, workspace=workspace, O=O, LSE=LSE)
     _check(lib().msa_decode_fwd_paged(ctypes.byref(desc), page, num_pages, _ptr(block_table), _ptr(ctx_lens),
                                       _ptr(q), _ptr(Kpages), _ptr(Vpages), _ptr(Kbar), _ptr(Vbar), _ptr(workspace),
                                       ws_bytes, _ptr(O), _ptr(LSE), _stream(q, stream)))
@@ -414,7 +530,17 @@ def msa_append_kv_paged(k_new, v_new, positions, Kpages, Vpages, block_table, Kb
     cap = block_table.shape[1] * page
     if cap >= 1 << 31:
         raise ValueError(f"capacity {cap} (pages per sequence x page) must be < 2^31 rows")
+    if k_new.dtype != Kpages.dtype or v_new.dtype != Kpages.dtype or Vpages.dtype != Kpages.dtype:
+        raise ValueError("new rows and page pools must share a dtype")
+    dev = Kpages.device
+    _expect(Kpages, "Kpages")
+    for t, name in ((Vpages, "Vpages"), (block_table, "block_table"), (positions, "positions"),
+                    (k_new, "k_new"), (v_new, "v_new")):
+        _expect(t, name)
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, Kpages.dtype)
     desc = decode_desc(B, Hkv, Hkv, cap, d, 1, num_landmarks, 1, 1.0, _dtype_code(Kpages.dtype))
+    _on_gpu(dev, Kpages=Kpages, Vpages=Vpages, block_table=block_table, positions=positions, k_new=k_new,
+            v_new=v_new, Kbar=Kbar, Vbar=Vbar)
     _check(lib().msa_append_kv_paged(ctypes.byref(desc), page, num_pages, _ptr(block_table), _ptr(positions),
                                      _ptr(k_new), _ptr(v_new), _ptr(Kpages), _ptr(Vpages), _ptr(Kbar), _ptr(Vbar),
                                      _stream(Kpages, stream)))
