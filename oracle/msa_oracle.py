@@ -536,12 +536,16 @@ def _mean_bwd(dXbar, L: int):
 
 
 def attn_bwd(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
-             kv_heads: Optional[Sequence[int]] = None, group_span: int = 512):
+             kv_heads: Optional[Sequence[int]] = None, group_span: int = 512, O=None):
     """Gradients (dQ [B, Hq, n, d], dK, dV [B, Hkv, n, d]) of the forward
     above, fp64, with landmarks the means of K and V.  ``kv_heads`` limits the
     work to those KV heads and their query heads (the other entries are
     zero).  Rows are processed in groups of nearby rows whose key range
-    strictly contains their windows, as in attn()."""
+    strictly contains their windows, as in attn().
+
+    ``O`` is the forward output the backward is handed (as a training step
+    saves it, e.g. rounded to bf16); it enters only through the softmax
+    term D_i = dO_i . O_i.  By default the exact forward output is used."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -575,8 +579,8 @@ def attn_bwd(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
                 ks, vs = K[b, g, lo:hi], V[b, g, lo:hi]
                 kb, vb = Kbar[b, g], Vbar[b, g]
                 P_win, P_lm, _ = _probs(scale * (q @ ks.T), M_win, scale * (q @ kb.T), M_lm)
-                O = P_win @ vs + P_lm @ vb
-                D = (do * O).sum(axis=1)
+                Or = P_win @ vs + P_lm @ vb if O is None else np.asarray(O[b, h, grp_rows], np.float64)
+                D = (do * Or).sum(axis=1)
                 dS_win = _softmax_bwd(P_win, do @ vs.T, D)
                 dS_lm = _softmax_bwd(P_lm, do @ vb.T, D)
                 dQ[b, h, grp_rows] = scale * (dS_win @ ks + dS_lm @ kb)
@@ -591,9 +595,11 @@ def attn_bwd(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
 
 
 def attn_bwd_dq_rows(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
-                     rows: Optional[Dict[int, np.ndarray]] = None, group_span: int = 512):
+                     rows: Optional[Dict[int, np.ndarray]] = None, group_span: int = 512, O=None):
     """dQ on selected rows only (dQ of a row needs only that row's visible
-    entries): {head: (rows, dQ [B, R, d])}."""
+    entries): {head: (rows, dQ [B, R, d])}.  ``O``, as in attn_bwd: the
+    forward output the backward is handed, {head: [B, R, d]} on the same
+    rows; by default the exact one."""
     Q = np.asarray(Q)
     B, Hq, n, d = Q.shape
     Hkv = K.shape[1]
@@ -621,8 +627,11 @@ def attn_bwd_dq_rows(Q, K, V, dO, w: int, G: int, scale: Optional[float] = None,
                 vs = np.asarray(V[b, g, lo:hi], np.float64)
                 kb, vb = kb_all[b], vb_all[b]
                 P_win, P_lm, _ = _probs(scale * (q @ ks.T), M_win, scale * (q @ kb.T), M_lm)
-                O = P_win @ vs + P_lm @ vb
-                D = (do * O).sum(axis=1)
+                if O is None:
+                    Or = P_win @ vs + P_lm @ vb
+                else:
+                    Or = np.asarray(O[h][b, pos:pos + len(grp_rows)], np.float64)
+                D = (do * Or).sum(axis=1)
                 dS_win = _softmax_bwd(P_win, do @ vs.T, D)
                 dS_lm = _softmax_bwd(P_lm, do @ vb.T, D)
                 res[b, pos:pos + len(grp_rows)] = scale * (dS_win @ ks + dS_lm @ kb)

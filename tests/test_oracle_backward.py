@@ -123,3 +123,34 @@ def test_kv_head_subset_matches_full():
     np.testing.assert_allclose(part[1][:, 1], full[1][:, 1], atol=1e-13)
     np.testing.assert_allclose(part[2][:, 1], full[2][:, 1], atol=1e-13)
     assert not part[0][:, :2].any() and not part[1][:, 0].any()
+
+
+@pytest.mark.parametrize("n,w,G", [(64, 9, 8), (40, 100, 0), (48, 5, 48)])
+def test_given_output_enters_through_d_only(n, w, G):
+    # The backward handed O + delta instead of the exact O changes the softmax
+    # term D_i = dO_i . O_i by dD_i = dO_i . delta_i and nothing else.  From
+    # dS = P (dP - D): dQ_i moves by -scale dD_i (P K)_i, where (P K)_i is the
+    # forward run with K as the values (landmarks of K are the key
+    # landmarks); dK moves by -scale times the value gradient that the
+    # upstream gradient dD_i q_i would give (dV = P^T dO has the same form,
+    # window and landmark scatter included); dV does not move.
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    Q, K, V = rnd((B, Hq, n, d), 120), rnd((B, Hkv, n, d), 121), rnd((B, Hkv, n, d), 122)
+    dO, delta = rnd((B, Hq, n, d), 123), 1e-3 * rnd((B, Hq, n, d), 124)
+    O_exact, _ = orc.attn_dense(Q, K, V, w, G, SC)
+    base = orc.attn_bwd(Q, K, V, dO, w, G, SC)
+    same = orc.attn_bwd(Q, K, V, dO, w, G, SC, O=O_exact)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    dQ1, dK1, dV1 = orc.attn_bwd(Q, K, V, dO, w, G, SC, O=O_exact + delta)
+    dD = (dO * delta).sum(axis=-1, keepdims=True)
+    PK, _ = orc.attn_dense(Q, K, K, w, G, SC)
+    np.testing.assert_allclose(dQ1 - base[0], -SC * dD * PK, atol=1e-13)
+    _, _, dV_of_dDq = orc.attn_bwd(Q, K, V, dD * Q, w, G, SC)
+    np.testing.assert_allclose(dK1 - base[1], -SC * dV_of_dDq, atol=1e-13)
+    np.testing.assert_allclose(dV1, base[2], atol=1e-13)
+    # the sampled-rows dQ takes the same given output on its rows
+    rows = {h: np.sort(np.random.default_rng(h).choice(n, 12, replace=False)) for h in (1, 2)}
+    Og = {h: (O_exact + delta)[:, h, r] for h, r in rows.items()}
+    for h, (r, dq) in orc.attn_bwd_dq_rows(Q, K, V, dO, w, G, SC, rows=rows, O=Og).items():
+        np.testing.assert_allclose(dq, dQ1[:, h, r], atol=1e-13)

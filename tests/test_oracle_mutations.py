@@ -139,6 +139,11 @@ def _row_plan_lo_from_top(n, w, G, rows=None):     # lowest visible key read fro
     return np.where(r - lo + 1 > 1, r, lo), cnt
 
 
+def _bwd_ignores_given_output(Q, K, V, dO, w, G, scale=None, kv_heads=None, group_span=512, O=None):
+    # forms D from the exact forward output even when handed another one
+    return orc.__dict__["_orig_attn_bwd"](Q, K, V, dO, w, G, scale, kv_heads, group_span)
+
+
 def _chunk_bounds_floor(E, S):                     # floor(E/S) entries per chunk
     s = E // S
     return np.array([min(E, c * s) for c in range(S)] + [E], dtype=np.int64)
@@ -166,6 +171,7 @@ MUTANTS = {
     "tile_k_hi_short": ("tile_plan", _tile_plan_variant(k_hi_short=True)),
     "row_plan_lo_from_top": ("row_plan", _row_plan_lo_from_top),
     "chunk_bounds_floor": ("chunk_bounds", _chunk_bounds_floor),
+    "bwd_ignores_given_output": ("attn_bwd", _bwd_ignores_given_output),
 }
 
 PIN_SET = [
@@ -192,6 +198,7 @@ PIN_SET = [
     lambda: plan.test_row_plan_equals_brute_force(300, 63, 10),
     lambda: plan.test_chunk_bounds_decode_workload(),
     lambda: plan.test_chunk_bounds_with_empty_chunks(),
+    lambda: bwd.test_given_output_enters_through_d_only(64, 9, 8),
 ]
 
 
@@ -219,5 +226,6 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(orc.__dict__, "_orig_pool_prefix", orc.pool_prefix)
     monkeypatch.setitem(orc.__dict__, "_orig_bs_mask", orc.blocksparse_mask)
     monkeypatch.setitem(orc.__dict__, "_orig_row_plan", orc.row_plan)
+    monkeypatch.setitem(orc.__dict__, "_orig_attn_bwd", orc.attn_bwd)
     monkeypatch.setattr(orc, attr, fn)
     assert _failures() > 0, f"no pin caught the planted mistake {name}"
