@@ -100,7 +100,64 @@ def summarize_pmc(fetch_csv, write_csv):
         with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         out[key] = rec
+    # pooling: the cache's landmarks (137 GB read) and the prefill's (0.54 GB), told apart by size
+    pf = {d: v for d, (name, v) in fetch.items() if "pool_kernel" in name}
+    pw = {d: v for d, (name, v) in write.items() if "pool_kernel" in name}
+    for key, big in (("pool_cache_512k", True), ("pool_prefill_128k", False)):
+        fd = [v * 1024.0 * fs for v in pf.values() if (v * 1024.0 * fs > 1e10) == big]
+        wd = [v * 1024.0 * ws for d, v in pw.items() if d in pf and (pf[d] * 1024.0 * fs > 1e10) == big]
+        if not fd or not wd:
+            continue
+        rec = {"source_hash": kernel_hash("pool.hip", "msa_device.hpp"), "fetch_bytes": sum(fd) / len(fd),
+               "write_bytes": sum(wd) / len(wd), "bytes_per_launch": sum(fd) / len(fd) + sum(wd) / len(wd),
+               "fetch_scale": fs, "write_scale": ws, "launches": len(fd)}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        out[key] = rec
     print(json.dumps(out, indent=1))
+
+
+ATTN_SRCS = ["attn_bf16.hip", "msa_plan.hpp", "msa_device.hpp"]
+
+
+def summarize_util(csv_path):
+    """Matrix-core utilisation and shader clock of the 128K prefill kernel
+    from a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run of
+    this bench: busy cycles over (1024 SIMDs x cycles of the launch), at the
+    clock the launch actually ran (GRBM_GUI_ACTIVE is summed over the 8
+    XCDs) and at the 2.4 GHz nominal clock."""
+    import csv
+
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if "attn_fwd_bf16_kernel<128, true>" not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    rows = [d for d in per.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d]
+    busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in rows) / len(rows)
+    cyc = sum(d["GRBM_GUI_ACTIVE"] / 8.0 for d in rows) / len(rows)
+    ns = sum(d["ns"] for d in rows) / len(rows)
+    rec = {"source_hash": kernel_hash(*ATTN_SRCS), "launches": len(rows), "launch_ms": ns / 1e6,
+           "clock_ghz": cyc / ns, "mfma_busy_cycles": busy,
+           "mfma_util_at_clock": busy / (1024.0 * cyc), "mfma_util_at_nominal": busy / (1024.0 * 2.4 * ns)}
+    with open(os.path.join(ROOT, "profiles", "util_attn_fwd_gqa_128k.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def util_from_profiles():
+    """The prefill's matrix-core utilisation from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "util_attn_fwd_gqa_128k.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_hash(*ATTN_SRCS):
+        return None
+    return {k: round(rec[k], 4) for k in ("mfma_util_at_clock", "mfma_util_at_nominal", "clock_ghz")}
 
 
 def visible_pairs(n, w, G):
@@ -343,6 +400,41 @@ def blocksparse_band_128k(torch, msa, wl, dev, stream, reps=3):
             "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
 
 
+def blocksparse_global_local_128k(torch, msa, wl, dev, stream, reps=3):
+    """Secondary line: msa_attn_fwd_blocksparse on the 128K GQA shapes with
+    global + local lists (non-causal): the first two 128-token blocks attend
+    to every key and every block attends to them; the other blocks see a
+    16-block local band.  FLOPs: 4*d per (row, listed key) pair."""
+    cfg = wl.GQA_128K
+    Q, K, V = wl.device_prefill_inputs(cfg, dev)
+    counts, idx = wl.global_local_block_lists(cfg.batch, cfg.heads_q, cfg.seq_len)
+    cd, id_ = torch.from_numpy(counts).to(dev), torch.from_numpy(idx).to(dev)
+    O = torch.empty_like(Q)
+    LSE = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    run = lambda: msa.msa_attn_fwd_blocksparse(Q, K, V, cd, id_, False, cfg.scale, O=O, LSE=LSE)
+    run()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        run()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / reps
+    n = cfg.seq_len
+    rows_per_tile = [min(n, (t + 1) * 128) - t * 128 for t in range(counts.shape[2])]
+    keys_per_tile = [sum(min(n, (kb + 1) * 64) - kb * 64 for kb in idx[0, 0, t, :counts[0, 0, t]])
+                     for t in range(counts.shape[2])]
+    pairs = sum(k * r for k, r in zip(keys_per_tile, rows_per_tile))
+    flops = 4.0 * cfg.head_dim * pairs * cfg.heads_q * cfg.batch
+    del Q, K, V, O, LSE, cd, id_
+    torch.cuda.empty_cache()
+    return {"workload": "gqa_128k shapes, block-sparse lists: global + local (2 global 128-token blocks that attend "
+                        "to all and are attended by all, 16-block local band, non-causal)", "ms": round(ms, 3),
+            "flops_per_launch": flops, "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": reps}
+
+
 def paged_decode(torch, msa, wl, dev, stream, page=64, reps=5):
     """Secondary line: the incremental-decode step on paged caches -- pools of
     64-row pages, each sequence's pages scattered by a seeded permutation --
@@ -425,10 +517,22 @@ def measured_peaks(torch, dev, reps=10):
     e[1].record()
     torch.cuda.synchronize()
     copy = 2.0 * x.numel() * 2 / (e[0].elapsed_time(e[1]) / reps * 1e-3) / 1e9
-    del x, y
+    del y
+    # read-only stream: a float32-accumulated sum over the same 2 GiB (writes one scalar)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(x, dtype=torch.float32, out=sink)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(reps):
+        torch.sum(x, dtype=torch.float32, out=sink)
+    e[1].record()
+    torch.cuda.synchronize()
+    read = x.numel() * 2 / (e[0].elapsed_time(e[1]) / reps * 1e-3) / 1e9
+    del x, sink
     torch.cuda.empty_cache()
     return {"bf16_gemm_tflops": round(gemm, 1), "bf16_gemm_shape": "8192^3 (torch.matmul)",
-            "hbm_copy_gbs": round(copy, 1), "hbm_copy": "2 GiB device copy, read + write bytes"}
+            "hbm_copy_gbs": round(copy, 1), "hbm_copy": "2 GiB device copy, read + write bytes",
+            "hbm_read_gbs": round(read, 1), "hbm_read": "float32-accumulated torch.sum over 2 GiB of bf16, bytes read"}
 
 
 def main():
@@ -450,9 +554,15 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run into "
                          "profiles/traffic_*.json and print the summary; runs nothing on the GPU")
+    ap.add_argument("--summarize-util", metavar="CSV",
+                    help="turn a rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE counter CSV of a bench run "
+                         "into profiles/util_attn_fwd_gqa_128k.json; runs nothing on the GPU")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_util:
+        summarize_util(args.summarize_util)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).",
@@ -583,8 +693,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profiles("attn_fwd_gqa_128k", ["attn_bf16.hip", "msa_plan.hpp",
-                                                                   "msa_device.hpp"]),
+            "traffic": traffic_from_profiles("attn_fwd_gqa_128k", ATTN_SRCS),
+            "mfma_util": util_from_profiles(),
             "flops_per_launch": flops,
             "avg_launch_ms": round(attn_ms, 4),
         },
@@ -602,8 +712,12 @@ def main():
         "pool": {
             "prefill_ms": round(pool_ms, 4),
             "prefill_GBps": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+            "prefill_bytes_per_launch": pool_bytes,
+            "prefill_traffic": traffic_from_profiles("pool_prefill_128k", ["pool.hip", "msa_device.hpp"]),
             "cache_ms": round(cache_pool_ms, 4),
             "cache_GBps": round(cache_bytes / (cache_pool_ms * 1e-3) / 1e9, 1),
+            "cache_bytes_per_launch": cache_bytes,
+            "cache_traffic": traffic_from_profiles("pool_cache_512k", ["pool.hip", "msa_device.hpp"]),
         },
         "kernels_ms": {"pool": stats(pool_t), "attn_fwd": stats(attn_t), "decode": stats(dec_t)},
         "useful_pairs_per_head": {"window": win_pairs, "landmark": lm_pairs},
@@ -623,11 +737,14 @@ def main():
         out["backward"] = backward_128k(torch, msa, wl, dev, stream)
     if not args.no_blocksparse:
         out["blocksparse"] = blocksparse_band_128k(torch, msa, wl, dev, stream)
+        out["blocksparse_global_local"] = blocksparse_global_local_128k(torch, msa, wl, dev, stream)
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
         out["measured_peaks"] = peaks
         out["roofline"]["frac_of_measured"] = round(attn_tflops / peaks["bf16_gemm_tflops"], 4)
-        out["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / peaks["hbm_copy_gbs"], 4)
+        # decode only reads: its reference is the read-only stream
+        out["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / peaks["hbm_read_gbs"], 4)
+        out["decode"]["roofline"]["measured_reference"] = "hbm_read_gbs"
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, Q, K, V, args.cpu_rows, list(range(8)))
     print(json.dumps(out), flush=True)

@@ -200,6 +200,37 @@ def band_block_lists(batch: int, heads: int, n: int, blocks: int = 16, block_tok
     return counts, idx
 
 
+def global_local_block_lists(batch: int, heads: int, n: int, global_blocks: int = 2, local_blocks: int = 16,
+                             block_tokens: int = 128, query_block: int = 128, key_block: int = 64):
+    """Block lists of the global + local pattern: global tokens that attend
+    to every token and that every token attends to, plus a local sliding
+    window ("Training at 1M+ Token Context: Ring Attention, YaRN, NTK-Aware
+    Scaling GPU Cost", Block-Sparse Flash Attention paragraph), at block
+    granularity and without a causal mask.  The first `global_blocks`
+    128-token blocks are the global tokens: their query blocks list every
+    key block; every other query block t lists the global blocks and the
+    128-token blocks t - local_blocks/2 .. t + local_blocks/2 - 1 (clipped,
+    each block once), as key_block-sized indices in ascending order.
+    Returns (counts int32 [B][H][T], indices int32 [B][H][T][max_blocks])."""
+    T = -(-n // query_block)
+    per = block_tokens // key_block
+    nkb = -(-n // key_block)
+    nblk = -(-n // block_tokens)
+    counts = np.zeros((batch, heads, T), np.int32)
+    idx = np.full((batch, heads, T, nkb), -1, np.int32)
+    for t in range(T):
+        c0 = t * query_block // block_tokens
+        if c0 < global_blocks:
+            blks = list(range(nblk))
+        else:
+            blks = sorted(set(range(min(global_blocks, nblk))) |
+                          {c for c in range(c0 - local_blocks // 2, c0 + local_blocks // 2) if 0 <= c < nblk})
+        kbs = [kb for c in blks for kb in range(c * per, (c + 1) * per) if kb < nkb]
+        counts[:, :, t] = len(kbs)
+        idx[:, :, t, :len(kbs)] = kbs
+    return counts, idx
+
+
 def random_block_lists(batch: int, heads: int, n: int, max_blocks: int, seed: int,
                        query_block: int = 128, key_block: int = 64):
     """Seeded random lists for tests: counts uniform in [0, max_blocks],

@@ -1,7 +1,8 @@
 """GPU parity of msa_attn_fwd_blocksparse (attention over listed 64-key
 blocks per 128-row query block) through the C ABI against the fp64 oracle:
 every row on small random lists (out-of-range and repeated indices, empty
-lists, causal and not), sampled rows on the 128K band pattern."""
+lists, causal and not), sampled rows on the 128K band pattern and on the
+128K global + local pattern."""
 import math
 
 import numpy as np
@@ -84,3 +85,33 @@ def test_blocksparse_band_128k():
         ridx = torch.from_numpy(r).to(dev())
         assert_close(host64(O32[:, h].index_select(1, ridx)), host64(L32[:, h].index_select(1, ridx)), o_ref, l_ref,
                      TOL_BF16, f"band 128k head {h} ({len(r)} rows)")
+
+
+def test_blocksparse_global_local_128k():
+    """Global + local lists at the 128K GQA shapes (non-causal): the first two
+    128-token blocks attend to every key and every block attends to them,
+    the rest see a 16-block local band.  Lists of very unequal length (2048
+    key blocks for the global rows, 20-36 for the others); rows of the
+    global blocks are graded among the sampled ones."""
+    cfg = wl.GQA_128K
+    print(f"[case] blocksparse global + local pattern on {cfg.name}", flush=True)
+    Q, K, V = wl.device_prefill_inputs(cfg, dev())
+    counts, idx = wl.global_local_block_lists(cfg.batch, cfg.heads_q, cfg.seq_len)
+    cd, id_ = torch.from_numpy(counts).to(dev()), torch.from_numpy(idx).to(dev())
+    O32, L32 = msa.msa_attn_fwd_blocksparse(Q, K, V, cd, id_, False, cfg.scale, out_dtype=torch.float32)
+    O16, _ = msa.msa_attn_fwd_blocksparse(Q, K, V, cd, id_, False, cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(O16, bf16_rne(O32))
+    grp = cfg.heads_q // cfg.heads_kv
+    for h in (0, 40, 63):
+        g = h // grp
+        rows = np.unique(np.concatenate([wl.sample_rows(cfg.seq_len, h, count=256),
+                                         np.array([3, 127, 128, 200, 255, 256, 257, 1100])]))
+        res = orc.attn_blocksparse_rows(host64(Q[:, h:h + 1]), host64(K[:, g:g + 1]), host64(V[:, g:g + 1]),
+                                        counts[:, h:h + 1], idx[:, h:h + 1], BQ, BK, False, cfg.scale,
+                                        rows={0: rows})
+        r, o_ref, l_ref = res[0]
+        ridx = torch.from_numpy(r).to(dev())
+        assert_close(host64(O32[:, h].index_select(1, ridx)), host64(L32[:, h].index_select(1, ridx)), o_ref, l_ref,
+                     TOL_BF16, f"global+local 128k head {h} ({len(r)} rows)")
+    del Q, K, V, O32, L32, O16, cd, id_
