@@ -601,7 +601,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   if (LSE != nullptr && lane == 0) LSE[bh] = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
 
-// Compute units of the current device (cached per device).
 // Compute units of the current device, cached per device (relaxed atomics:
 // concurrent first calls on several threads store the same value).
 int device_cus() {
