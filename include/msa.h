@@ -58,7 +58,7 @@ extern "C" {
  * the paged msa_decode_fwd_paged, msa_append_kv_paged),
  * the backward (msa_attn_bwd_workspace_size, msa_attn_bwd) and block-sparse
  * lists (msa_attn_fwd_blocksparse). */
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 typedef enum {
   MSA_OK = 0,
@@ -227,6 +227,30 @@ msa_status msa_decode_workspace_size(const msa_decode_desc* desc, size_t* bytes)
 msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void* Kcache,
                           const void* Vcache, const void* Kbar, const void* Vbar, void* workspace,
                           size_t workspace_bytes, void* O, float* LSE, void* stream);
+
+/* Bytes of the library's own device array behind msa_decode_fwd_noalloc. */
+#define MSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* msa_decode_fwd without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it.  Arguments, results
+ * and errors are those of msa_decode_fwd minus the workspace; the caller
+ * still provides q, the caches, the landmarks, O and LSE.  The split
+ * schedule's per-chunk partials go to a static device array inside the
+ * library, MSA_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held
+ * until the process ends; a problem that runs the split schedule and needs
+ * more (num_splits * batch * heads_q * (head_dim + 1) * 4 bytes) is
+ * rejected with MSA_ERR_WORKSPACE before any launch (the fused schedule
+ * needs none).  Every call on a GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that overlap on one GPU (different streams,
+ * threads) race, and the caller must serialise them.  Nothing in the array
+ * needs clearing: each call overwrites every partial its merge reads.  The
+ * array's device address is looked up once per device, on the first call
+ * with that device current.  Calls no hipMalloc, hipFree or allocating
+ * routine. */
+msa_status msa_decode_fwd_noalloc(const msa_decode_desc* desc, const void* q, const void* Kcache,
+                                  const void* Vcache, const void* Kbar, const void* Vbar, void* O,
+                                  float* LSE, void* stream);
 
 /* ---- Incremental decode: sequences of different lengths in one cache,
  * grown one token per step.  The pages run generation after a long prompt

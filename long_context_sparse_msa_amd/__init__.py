@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     msa_attn_fwd_blocksparse,
     msa_append_kv_paged,
     msa_decode_fwd,
+    msa_decode_fwd_noalloc,
     msa_decode_fwd_paged,
     msa_decode_fwd_varlen,
     msa_decode_workspace_size,

@@ -32,7 +32,7 @@ EXPORTS = (
     "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_status_string",
     "msa_last_error", "msa_abi_version", "msa_decode_fwd_varlen", "msa_append_kv",
     "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd", "msa_attn_fwd_blocksparse",
-    "msa_decode_fwd_paged", "msa_append_kv_paged",
+    "msa_decode_fwd_paged", "msa_append_kv_paged", "msa_decode_fwd_noalloc",
 )
 
 LIST_QUERY_BLOCK = 128
@@ -102,10 +102,12 @@ def lib() -> ctypes.CDLL:
         L.msa_decode_fwd_paged.argtypes = [P(DecodeDesc), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.msa_append_kv_paged.argtypes = [P(DecodeDesc), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_attn_bwd.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
+        L.msa_decode_fwd_noalloc.argtypes = [P(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         for f in ("msa_pool_landmarks", "msa_attn_fwd", "msa_decode_workspace_size", "msa_decode_fwd",
                   "msa_plan_rows", "msa_plan_tiles", "msa_plan_decode", "msa_decode_fwd_varlen",
                   "msa_append_kv", "msa_plan_decode_varlen", "msa_attn_bwd_workspace_size", "msa_attn_bwd",
-                  "msa_attn_fwd_blocksparse", "msa_decode_fwd_paged", "msa_append_kv_paged"):
+                  "msa_attn_fwd_blocksparse", "msa_decode_fwd_paged", "msa_append_kv_paged",
+                  "msa_decode_fwd_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -400,6 +402,40 @@ def msa_decode_fwd(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_s
     _on_gpu(dev, q=q, Kc=Kc, Vc=Vc, Kbar=Kbar, Vbar=Vbar, workspace=workspace, O=O, LSE=LSE)
     _check(lib().msa_decode_fwd(ctypes.byref(desc), _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(Kbar), _ptr(Vbar),
                                 _ptr(workspace), ws_bytes, _ptr(O), _ptr(LSE), _stream(q, stream)))
+    return O, LSE
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def msa_decode_fwd_noalloc(q, Kc, Vc, Kbar, Vbar, window: int, num_landmarks: int, num_splits: int,
+                           scale: Optional[float] = None, O=None, LSE=None, stream=None, schedule=None):
+    """msa_decode_fwd without a workspace: the split schedule's partials live
+    in the library's own device array (NOALLOC_SCRATCH_BYTES per GPU).  For
+    callers that cannot allocate, pass O (and LSE); the library allocates
+    nothing.  Overlapping calls on one GPU race on that array."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, ctx = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, ctx, d) or Vc.shape != Kc.shape:
+        raise ValueError("cache shapes do not match q")
+    if Kc.dtype != q.dtype or Vc.dtype != q.dtype:
+        raise ValueError("q and the caches must share a dtype")
+    in_code = _dtype_code(q.dtype)
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    out_code = _dtype_code(O.dtype)
+    dev = q.device
+    _expect(q, "q")
+    _expect(Kc, "Kc")
+    _expect(Vc, "Vc")
+    _expect_landmarks(Kbar, Vbar, B, Hkv, num_landmarks, d, q.dtype)
+    _expect(O, "O", (B, Hq, d), _torch_dtype(out_code))
+    _expect(LSE, "LSE", (B, Hq), torch.float32, optional=True)
+    desc = decode_desc(B, Hq, Hkv, ctx, d, window, num_landmarks, num_splits, scale, in_code, out_code, schedule)
+    _on_gpu(dev, q=q, Kc=Kc, Vc=Vc, Kbar=Kbar, Vbar=Vbar, O=O, LSE=LSE)
+    _check(lib().msa_decode_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(Kbar), _ptr(Vbar),
+                                        _ptr(O), _ptr(LSE), _stream(q, stream)))
     return O, LSE
 
 

@@ -304,6 +304,31 @@ msa_status msa_decode_fwd(const msa_decode_desc* desc, const void* q, const void
                     "decode launch");
 }
 
+msa_status msa_decode_fwd_noalloc(const msa_decode_desc* desc, const void* q, const void* Kcache,
+                                  const void* Vcache, const void* Kbar, const void* Vbar, void* O, float* LSE,
+                                  void* stream) {
+  msa_status s = check_decode(desc);
+  if (s != MSA_OK) return s;
+  if (desc->batch == 0) return ok();
+  if ((s = check_ptr(q, "q")) || (s = check_ptr(Kcache, "Kcache")) || (s = check_ptr(Vcache, "Vcache")) ||
+      (s = check_ptr(O, "O")))
+    return s;
+  if (desc->num_landmarks > 0 && ((s = check_ptr(Kbar, "Kbar")) || (s = check_ptr(Vbar, "Vbar")))) return s;
+  if (LSE != nullptr && !aligned16(LSE)) return fail(MSA_ERR_INVALID_ARG, "LSE is not 16-byte aligned");
+  const size_t need = decode_ws_bytes(desc);
+  if (desc->schedule != MSA_DECODE_FUSED && need > msa::kNoallocScratchBytes && msa::decode_uses_split(*desc))
+    return fail(MSA_ERR_WORKSPACE, "the split schedule needs %zu bytes of partials, more than the %zu of the "
+                                   "library's array (use msa_decode_fwd with a workspace)",
+                need, (size_t)msa::kNoallocScratchBytes);
+  float* ws = nullptr;
+  hipError_t e = msa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
+  float* ws_lse = ws + (size_t)desc->num_splits * desc->batch * desc->heads_q * desc->head_dim;
+  return hip_status(msa::launch_decode(*desc, q, Kcache, Vcache, Kbar, Vbar, nullptr, nullptr, ws, ws_lse, O, LSE,
+                                       static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
 msa_status msa_decode_fwd_varlen(const msa_decode_desc* desc, const int32_t* ctx_lens, const void* q,
                                  const void* Kcache, const void* Vcache, const void* Kbar, const void* Vbar,
                                  void* workspace, size_t workspace_bytes, void* O, float* LSE, void* stream) {

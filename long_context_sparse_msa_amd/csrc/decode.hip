@@ -30,6 +30,7 @@
 //    (sequence, KV head, chunk) writes its partial; decode_merge_kernel
 //    then merges the chunks of each (sequence, query head).
 #include <atomic>
+#include <mutex>
 
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
@@ -675,6 +676,35 @@ hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc
   }
   return d.head_dim == 128 ? launch_t<128, false>(d, A, ws_o, ws_lse, O, LSE, stream)
                            : launch_t<64, false>(d, A, ws_o, ws_lse, O, LSE, stream);
+}
+
+bool decode_uses_split(const msa_decode_desc& d) { return !use_fused(d); }
+
+// Per-chunk partials of the allocation-free decode: a library-owned device
+// array, one copy on every GPU the library runs on, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel -- on the host
+// the name is only a stand-in -- but the device address that
+// hipGetSymbolAddress reports for the current device.  The split kernel
+// writes every (chunk, sequence, query head) slot the merge reads, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(float** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  return hipSuccess;
 }
 
 }  // namespace msa

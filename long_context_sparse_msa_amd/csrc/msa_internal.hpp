@@ -50,6 +50,16 @@ hipError_t launch_decode(const msa_decode_desc& d, const void* q, const void* Kc
                          const void* Kbar, const void* Vbar, const int32_t* lens, const DecodePaging* paging,
                          float* ws_o, float* ws_lse, void* O, float* LSE, hipStream_t stream);
 
+// Whether the decode of d runs the split schedule (per-chunk partials in
+// the workspace) rather than the fused one.
+bool decode_uses_split(const msa_decode_desc& d);
+
+// The allocation-free decode's partials: a static device array of
+// kNoallocScratchBytes; *ptr receives its address on the current device
+// (looked up once per device).
+constexpr size_t kNoallocScratchBytes = MSA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(float** ptr);
+
 // Write one token's K/V row per sequence at positions[b] (skipped outside
 // [0, ctx_len)) and re-pool the landmark block that row completes.
 hipError_t launch_append(const msa_decode_desc& d, const int32_t* positions, const DecodePaging* paging,

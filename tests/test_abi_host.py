@@ -31,14 +31,14 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(msa.EXPORTS) == names
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version(L):
-    assert msa.abi_version() == 2
+    assert msa.abi_version() == 3
 
 
 def test_status_strings(L):
@@ -400,3 +400,15 @@ def test_paged_append_validation():
     assert f(ctypes.byref(d), 64, 8, p, p, p, p, p, p, None, p, None) == 1   # Kbar needed with G > 0
     assert f(ctypes.byref(dec_desc(in_dtype=msa.MSA_DTYPE_F32)), 64, 8, p, p, p, p, p, p, p, p, None) == 2
     assert f(ctypes.byref(dec_desc(batch=0)), 48, 0, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_array():
+    # 64 sequences x 64 query heads x 16 chunks x 129 floats = 33,816,576 B of
+    # partials under the split schedule: more than the library's 32 MiB
+    d = dec_desc(batch=64, heads_q=64, heads_kv=8, ctx_len=4096, window=1024, num_landmarks=8, num_splits=16,
+                 schedule=msa.MSA_DECODE_SPLIT)
+    p = ctypes.c_void_p(16)
+    L = msa.lib()
+    assert L.msa_decode_fwd_noalloc(ctypes.byref(d), p, p, p, p, p, p, None, None) == 3  # MSA_ERR_WORKSPACE
+    assert b"33816576 bytes of partials" in L.msa_last_error()
+    assert L.msa_decode_fwd_noalloc(ctypes.byref(d), None, p, p, p, p, p, None, None) == 1
