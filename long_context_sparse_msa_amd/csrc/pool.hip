@@ -48,13 +48,6 @@ struct Chunk<float> {
   }
 };
 
-// Mean of the L rows of one block (row stride D elements) by one workgroup
-// of 256 threads, laid out as kRowLanes row lanes x kChunks 16-byte column
-// chunks: row lane rl sums rows rl, rl + kRowLanes, ... of the block in
-// ascending order, then the row lanes are added in order through LDS and
-// the sum divided by L.  With LAST, row L-1 is read from `last` instead of
-// the block (the row an append is writing), which gives the same bits as
-// pooling the block once that row is stored.  Called by every thread.
 template <typename T, int D>
 struct PoolShape {
   static constexpr int kE = Chunk<T>::kElems;
@@ -84,11 +77,24 @@ struct RowsPaged {
   }
 };
 
+// Mean of the L rows of one block (row stride D elements) by one workgroup
+// of 256 threads, laid out as kRowLanes row lanes x kChunks 16-byte column
+// chunks.  Row lane rl sums rows rl, rl + kRowLanes, ... of the block in
+// ascending order, issuing the loads of up to 16 of its rows before adding
+// any; the row lanes of each wavefront are then combined by a butterfly of
+// lane exchanges (both partners of an exchange form the same sum, addition
+// being commutative), the 4 wavefronts' sums are added in order through
+// LDS, and the total is divided by L.  The order is fixed, so the result is
+// deterministic.  With LAST, row L-1 is read from `last` instead of the
+// block (the row an append is writing), which gives the same bits as
+// pooling the block once that row is stored.  Called by every thread.
 template <typename T, int D, bool LAST, typename Rows>
 __device__ __forceinline__ void pool_block(const Rows& rows, const T* __restrict__ last, int L, T* __restrict__ dst,
-                                           float (*red)[D + 1]) {
+                                           float (*red)[D]) {
   using PS = PoolShape<T, D>;
   constexpr int kE = PS::kE, kChunks = PS::kChunks, kRowLanes = PS::kRowLanes;
+  constexpr int kBatch = 16;
+  static_assert(kChunks <= 64 && 64 % kChunks == 0, "a wavefront holds whole rows of chunks");
   const int ch = threadIdx.x % kChunks;
   const int rl = threadIdx.x / kChunks;
   float acc[kE];
@@ -100,6 +106,13 @@ __device__ __forceinline__ void pool_block(const Rows& rows, const T* __restrict
     return (LAST && r == L - 1) ? lp : reinterpret_cast<const u32x4*>(rows.row(r)) + ch;
   };
   int r = rl;
+  for (; r + (kBatch - 1) * kRowLanes < L; r += kBatch * kRowLanes) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) v[i] = *row(r + i * kRowLanes);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) Chunk<T>::add(acc, v[i]);
+  }
   for (; r + 3 * kRowLanes < L; r += 4 * kRowLanes) {
     const u32x4 a = *row(r);
     const u32x4 b = *row(r + kRowLanes);
@@ -112,16 +125,24 @@ __device__ __forceinline__ void pool_block(const Rows& rows, const T* __restrict
   }
   for (; r < L; r += kRowLanes) Chunk<T>::add(acc, *row(r));
 
+  // lanes l and l ^ (kChunks << k) hold the same chunk of other rows
 #pragma unroll
-  for (int e = 0; e < kE; ++e) red[rl][ch * kE + e] = acc[e];
+  for (int off = kChunks; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < kChunks) {
+#pragma unroll
+    for (int e = 0; e < kE; ++e) red[wave][ch * kE + e] = acc[e];
+  }
   __syncthreads();
   if (threadIdx.x < kChunks) {
     float out[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-      float s = 0.f;
-      for (int q = 0; q < kRowLanes; ++q) s += red[q][threadIdx.x * kE + e];
-      out[e] = s / (float)L;
+      const int c = threadIdx.x * kE + e;
+      out[e] = (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]) / (float)L;
     }
     Chunk<T>::store(dst + threadIdx.x * kE, out);
   }
@@ -132,7 +153,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                    T* __restrict__ Kbar, T* __restrict__ Vbar, int n,
                                                    int G, int L, int blocks_per_tensor) {
-  __shared__ float red[PoolShape<T, D>::kRowLanes][D + 1];
+  __shared__ float red[4][D];
   const int wg = blockIdx.x;
   const bool is_v = wg >= blocks_per_tensor;
   const int blk = is_v ? wg - blocks_per_tensor : wg;  // over batch*kv_heads*G
@@ -165,7 +186,7 @@ struct AppendArgs {
 
 template <int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs A) {
-  __shared__ float red[PoolShape<uint16_t, D>::kRowLanes][D + 1];
+  __shared__ float red[4][D];
   const int wg = blockIdx.x;
   const bool is_v = wg >= A.pairs;
   const int bk = is_v ? wg - A.pairs : wg;  // b * Hkv + kvh
