@@ -208,18 +208,17 @@ def gqa128k():
     O16, _ = run_attn(Q, K, V, cfg.window, cfg.num_landmarks, cfg.scale)
     torch.cuda.synchronize()
     assert torch.equal(O16, bf16_rne(O32))
-    del O16
-    yield cfg, Q, K, V, O32, L32
-    del Q, K, V, O32, L32
+    yield cfg, Q, K, V, O32, L32, O16
+    del Q, K, V, O32, L32, O16
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("g", range(8))
 def test_attn_128k_kv_group(gqa128k, g):
-    cfg, Q, K, V, O32, L32 = gqa128k
+    cfg, Q, K, V, O32, L32, O16 = gqa128k
     rows = {h: r for h, r in sampled(cfg).items() if h // 8 == g}
     check_rows(Q, K, V, O32, L32, cfg.window, cfg.num_landmarks, cfg.scale, rows, TOL_BF16,
-               f"{cfg.name} kv{g}")
+               f"{cfg.name} kv{g}", O16=O16)
 
 
 @pytest.fixture(scope="module")
@@ -231,18 +230,17 @@ def gqa1m():
     O16, _ = run_attn(Q, K, V, cfg.window, cfg.num_landmarks, cfg.scale)
     torch.cuda.synchronize()
     assert torch.equal(O16, bf16_rne(O32))
-    del O16
-    yield cfg, Q, K, V, O32, L32
-    del Q, K, V, O32, L32
+    yield cfg, Q, K, V, O32, L32, O16
+    del Q, K, V, O32, L32, O16
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("g", range(8))
 def test_attn_1m_kv_group(gqa1m, g):
-    cfg, Q, K, V, O32, L32 = gqa1m
+    cfg, Q, K, V, O32, L32, O16 = gqa1m
     rows = {h: r for h, r in sampled(cfg).items() if h // 8 == g}
     check_rows(Q, K, V, O32, L32, cfg.window, cfg.num_landmarks, cfg.scale, rows, TOL_BF16,
-               f"{cfg.name} kv{g}", group_span=4096)
+               f"{cfg.name} kv{g}", group_span=4096, O16=O16)
 
 
 def test_attn_compression_tokens_128k():
