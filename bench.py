@@ -491,6 +491,34 @@ def paged_decode(torch, msa, wl, dev, stream, page=64, reps=5):
             "bytes_per_launch": nbytes, "append_ms": round(app, 4), "launches": reps}
 
 
+def mfma_references():
+    """Matrix-core throughput of two fixed instruction streams, run by
+    libmsa_ref.so on this GPU (2048 workgroups, two wavefronts per SIMD,
+    random bf16 operands, best of 5 launches): MFMAs on register operands,
+    and the prefill's per-tile chain QK -> softmax -> PV with its LDS operand
+    reads and no HBM traffic."""
+    import ctypes
+
+    path = os.path.join(ROOT, "long_context_sparse_msa_amd", "libmsa_ref.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run long_context_sparse_msa_amd.build first")
+    lib = ctypes.CDLL(path)
+    lib.msa_ref_mfma.restype = ctypes.c_int
+    lib.msa_ref_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]
+    out = {}
+    for mode, key in ((0, "mfma_register_tflops"), (1, "mfma_chain_tflops")):
+        ms, flops = ctypes.c_double(), ctypes.c_double()
+        rc = lib.msa_ref_mfma(mode, 2000, 5, ctypes.byref(ms), ctypes.byref(flops))
+        if rc != 0:
+            raise RuntimeError(f"msa_ref_mfma(mode {mode}) failed with HIP error {rc}")
+        out[key] = round(flops.value / (ms.value * 1e-3) / 1e12, 1)
+    out["mfma_register"] = "32x32x16 bf16 MFMAs on register operands, four accumulators"
+    out["mfma_chain"] = ("per trip QK (16 MFMAs, A by ds_read_b128) -> exp2 of the 32 scores per lane, sums, "
+                         "packs, dot products -> PV (16 MFMAs, A by transpose reads), no HBM traffic")
+    return out
+
+
 def measured_peaks(torch, dev, reps=10):
     """Achievable references on this GPU through vendor libraries: a large
     bf16 GEMM (hipBLASLt) and a 2 GiB device copy (bytes read + written)."""
@@ -533,7 +561,9 @@ def measured_peaks(torch, dev, reps=10):
     read = x.numel() * 2 / (e[0].elapsed_time(e[1]) / reps * 1e-3) / 1e9
     del x, xv, sink
     torch.cuda.empty_cache()
-    return {"bf16_gemm_tflops": round(gemm, 1), "bf16_gemm_shape": "8192^3 (torch.matmul)",
+    torch.cuda.synchronize()
+    refs = mfma_references()
+    return {**refs, "bf16_gemm_tflops": round(gemm, 1), "bf16_gemm_shape": "8192^3 (torch.matmul)",
             "hbm_copy_gbs": round(copy, 1), "hbm_copy": "2 GiB device copy, read + write bytes",
             "hbm_read_gbs": round(read, 1), "hbm_read": "float32-accumulated torch.sum over 2 GiB of bf16 in rows of 4096, bytes read"}
 
@@ -762,6 +792,7 @@ def main():
         peaks = measured_peaks(torch, dev)
         out["measured_peaks"] = peaks
         out["roofline"]["frac_of_measured"] = round(attn_tflops / peaks["bf16_gemm_tflops"], 4)
+        out["roofline"]["frac_of_chain"] = round(attn_tflops / peaks["mfma_chain_tflops"], 4)
         # decode only reads: its reference is the read-only stream
         out["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / peaks["hbm_read_gbs"], 4)
         out["decode"]["roofline"]["measured_reference"] = "hbm_read_gbs"

@@ -3,8 +3,10 @@
     python -m long_context_sparse_msa_amd.build
 
 Every HIP source under csrc/ is compiled for gfx950 with hipcc and linked
-into long_context_sparse_msa_amd/libmsa.so.  Packed-fp32 instruction
-selection is disabled for all device code.
+into long_context_sparse_msa_amd/libmsa.so.  The measured references that
+bench.py reports beside the kernels (ref/, not part of libmsa's interface)
+go into libmsa_ref.so.  Packed-fp32 instruction selection is disabled for
+all device code.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
+REF_SRC = os.path.join(PKG, "ref", "mfma_ref.hip")
+REF_LIB = os.path.join(PKG, "libmsa_ref.so")
 ARCH = "gfx950"
 
 
@@ -83,9 +87,21 @@ def build(verbose: bool = False) -> str:
         os.remove(tmp)
         raise RuntimeError("link left kernel launch stubs undefined: " + ", ".join(stubs))
     os.replace(tmp, LIB)
+    build_ref()
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {REF_LIB}")
     return LIB
+
+
+def build_ref() -> str:
+    """Compile and link libmsa_ref.so (bench.py's measured references)."""
+    tmp = REF_LIB + ".tmp"
+    cmd = [hipcc()] + COMMON + ["-shared", REF_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {REF_SRC}:\n" + res.stdout + res.stderr)
+    os.replace(tmp, REF_LIB)
+    return REF_LIB
 
 
 if __name__ == "__main__":

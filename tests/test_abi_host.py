@@ -412,3 +412,22 @@ def test_noalloc_decode_rejects_partials_beyond_its_array():
     assert L.msa_decode_fwd_noalloc(ctypes.byref(d), p, p, p, p, p, p, None, None) == 3  # MSA_ERR_WORKSPACE
     assert b"33816576 bytes of partials" in L.msa_last_error()
     assert L.msa_decode_fwd_noalloc(ctypes.byref(d), None, p, p, p, p, p, None, None) == 1
+
+
+def test_reference_library_loads_and_rejects_bad_arguments():
+    """bench.py's measured references live in libmsa_ref.so, outside the
+    library's interface: it loads, exports msa_ref_mfma, and refuses a bad
+    mode or count before touching the GPU."""
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "long_context_sparse_msa_amd", "libmsa_ref.so")
+    if not os.path.exists(path):
+        pytest.skip("libmsa_ref.so not built")
+    ref = ctypes.CDLL(path)
+    f = ref.msa_ref_mfma
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                  ctypes.POINTER(ctypes.c_double)]
+    ms, fl = ctypes.c_double(), ctypes.c_double()
+    for mode, iters, reps in ((2, 10, 1), (-1, 10, 1), (0, 0, 1), (1, 10, 0)):
+        assert f(mode, iters, reps, ctypes.byref(ms), ctypes.byref(fl)) != 0
+    assert f(0, 10, 1, None, ctypes.byref(fl)) != 0
