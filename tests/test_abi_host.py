@@ -431,3 +431,48 @@ def test_reference_library_loads_and_rejects_bad_arguments():
     for mode, iters, reps in ((2, 10, 1), (-1, 10, 1), (0, 0, 1), (1, 10, 0)):
         assert f(mode, iters, reps, ctypes.byref(ms), ctypes.byref(fl)) != 0
     assert f(0, 10, 1, None, ctypes.byref(fl)) != 0
+
+
+def _random_shapes(count, seed):
+    """Seeded (n, w, G) with G = 0 or a divisor of n (n = G * L), windows from
+    1 to beyond n, and n from 1 to a few thousand."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        L = int(rng.integers(1, 300))
+        G = int(rng.integers(0, 24))
+        n = G * L if G > 0 else int(rng.integers(1, 5000))
+        if n < 1 or n > 6000:
+            continue
+        w = int(rng.choice([1, 2, 63, 64, 65, int(rng.integers(1, n + 1)), n, 2 * n + 3]))
+        out.append((n, max(1, w), G))
+    return out
+
+
+@pytest.mark.parametrize("n,w,G", _random_shapes(60, 11))
+def test_plan_rows_and_tiles_bitexact_random(n, w, G):
+    """Seeded random shapes (ragged n, landmark blocks of any length, windows
+    shorter and longer than n): the library's row and tile plans equal the
+    oracle's mask-derived ones exactly."""
+    d = base_desc(seq_len=n, window=w, num_landmarks=G)
+    win_lo, lm = msa.msa_plan_rows(d)
+    rows = np.arange(n)
+    o_lo, o_lm = orc.row_plan(n, w, G, rows)
+    np.testing.assert_array_equal(win_lo, o_lo)
+    np.testing.assert_array_equal(lm, o_lm)
+    tiles, bm, bn = msa.msa_plan_tiles(d)
+    T = -(-n // bm)
+    want = orc.tile_plan(n, w, G, bm, bn, q_tiles=list(range(T)))
+    got = [tuple(int(x) for x in r[:3]) + (bool(r[3]),) for r in tiles]
+    assert got == want
+
+
+@pytest.mark.parametrize("ctx,w,G,S", [(s[0], s[1], s[2], int(k)) for s, k in
+                                       zip(_random_shapes(40, 12), np.random.default_rng(13).integers(1, 40, 40))])
+def test_plan_decode_bitexact_random(ctx, w, G, S):
+    d = dec_desc(ctx_len=ctx, window=w, num_landmarks=G, num_splits=S)
+    bounds, lm, ent = msa.msa_plan_decode(d)
+    kinds, idx = orc.visible_list(ctx - 1, ctx, w, G)
+    assert ent == len(idx)
+    assert lm == int((kinds == 0).sum())
+    np.testing.assert_array_equal(bounds, orc.chunk_bounds(len(idx), S))
